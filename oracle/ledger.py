@@ -1,0 +1,60 @@
+"""Training-state bytes per parameter under data parallelism and ZeRO stages.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The ledger of mixed-precision Adam training ("CS336 2026 Lecture 8:
+Parallelism Basics", Slide 17; "并行策略总览：六个维度各切什么、怎么通信",
+data-parallel section): a 16-bit parameter (2 B), a 16-bit gradient (2 B),
+an fp32 master copy (4 B) and Adam's first and second moments (4 B each),
+16 bytes per parameter in all.  ZeRO shards these over the N data-parallel
+ranks stage by stage (Lecture 8, ZeRO stage table and Slides 19-25):
+stage 1 shards the optimizer state (master, m, v), stage 2 also the
+gradients, stage 3 also the parameters.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+
+@dataclasses.dataclass(frozen=True)
+class Ledger:
+    param: float        # bytes per parameter of the working (16-bit) weights
+    grad: float         # bytes per parameter of the gradient
+    optimizer: float    # bytes per parameter of optimizer state (master + m + v)
+
+    @property
+    def total(self) -> float:
+        return self.param + self.grad + self.optimizer
+
+    def per_rank_bytes_per_param(self, stage: int, n_ranks: int) -> float:
+        """Bytes each rank holds per model parameter.  stage 0 = plain DP."""
+        p, g, o, n = self.param, self.grad, self.optimizer, float(n_ranks)
+        if stage == 0:
+            return p + g + o
+        if stage == 1:
+            return p + g + o / n
+        if stage == 2:
+            return p + (g + o) / n
+        if stage == 3:
+            return (p + g + o) / n
+        raise ValueError(stage)
+
+    def max_params(self, hbm_bytes: float, stage: int, n_ranks: int) -> float:
+        """Largest model whose training state fits one rank's memory."""
+        return hbm_bytes / self.per_rank_bytes_per_param(stage, n_ranks)
+
+
+# bf16 parameter + bf16 gradient + fp32 master, m, v.
+MIXED_PRECISION_ADAM = Ledger(param=2, grad=2, optimizer=4 + 4 + 4)
+
+# Element sizes of the arrays the shard step reads and writes: bf16 param
+# slot, bf16 gradient partial, fp32 master, fp32 m, fp32 v.
+STATE_ELEMENT_BYTES = {"param": 2, "grad": 2, "master": 4, "m": 4, "v": 4}
+
+
+def shard_step_bytes_per_param(n_ranks: int, grad_bytes: int = 2) -> int:
+    """HBM bytes the fused step must move per shard element: read N gradient
+    partials and the fp32 master, m, v; write master, m, v and the 16-bit
+    parameter."""
+    s = STATE_ELEMENT_BYTES
+    return n_ranks * grad_bytes + 2 * (s["master"] + s["m"] + s["v"]) + s["param"]

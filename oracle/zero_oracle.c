@@ -1,0 +1,230 @@
+/*
+ * CPU ORACLE of one data-parallel rank's sharded optimizer step.
+ * TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load it.  The GPU library never links, loads or calls it,
+ * and it shares no code, header or table with that library.
+ *
+ * What it computes, and where the pages define it:
+ *
+ *  - Shard ownership.  The parameters are one flat vector (the tensor list
+ *    concatenated in order); with N data-parallel ranks, rank r owns the
+ *    contiguous segment [r*S, (r+1)*S), S = ceil(total / N), the last
+ *    segment possibly shorter.  Each rank updates one segment only and
+ *    the segments together cover every parameter once ("CS336 2026
+ *    Lecture 8: Parallelism Basics", Slides 19-20: each rank is responsible
+ *    for one segment of the parameters and keeps only that segment's Adam
+ *    state; "并行训练优化、MoE扩展与系统瓶颈", 2.2.1).
+ *
+ *  - Reduce.  The gradient of the shard is the average of the N ranks'
+ *    local gradients, g = (1/N) * sum_k g_k ("并行策略总览：六个维度各切什么、
+ *    怎么通信", data-parallel section, the gradient-averaging identity;
+ *    CS231n "Large-Scale Distributed Training" notes, 4.1).  Reduce-scatter
+ *    delivers exactly the owner's slice of the all-reduce result (Lecture 8,
+ *    Slide 8: all-reduce = reduce-scatter + all-gather).  The sum is taken
+ *    in double, rank 0 first, adding ranks 1..N-1 in order, then divided
+ *    by N; the reduced shard is handed to the optimizer as an fp32 tensor.
+ *
+ *  - AdamW.  The pages name the optimizer state (fp32 master weights, Adam
+ *    first moment m and second moment v, Lecture 8 Slide 17) but never write
+ *    the update.  The reading taken is decoupled-weight-decay Adam
+ *    (Loshchilov & Hutter) with bias correction, eps outside the root:
+ *        m' = b1 m + (1 - b1) g
+ *        v' = b2 v + (1 - b2) g^2
+ *        mhat = m' / (1 - b1^t),  vhat = v' / (1 - b2^t)
+ *        theta' = theta (1 - lr wd) - lr mhat / (sqrt(vhat) + eps)
+ *    every operation in IEEE double, each stored result rounded once to
+ *    fp32 (round-to-nearest-even).
+ *
+ *  - Parameter write.  The bf16 parameter is the fp32 master rounded to
+ *    nearest-even bf16 (mixed precision keeps 16-bit parameters beside the
+ *    fp32 master, Lecture 8 Slide 17), written into the rank's slot of the
+ *    full parameter buffer: the local half of the parameter all-gather
+ *    (Lecture 8 Slide 20, fourth step).  NaN stays NaN (quiet bit set,
+ *    sign kept); overflow rounds to infinity.
+ *
+ * The storage formats (bf16 parameters and gradient partials, fp32 master,
+ * m, v) are the ones the pages fix in the 16-bytes-per-parameter ledger
+ * (Lecture 8 Slide 17); the arithmetic precision is not fixed there, so
+ * the oracle computes in double.
+ *
+ * Built with gcc -O2 -ffp-contract=off -fno-fast-math: no fused
+ * multiply-add, IEEE double on SSE2, correctly rounded sqrt and division.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_BF16 = 0, ORACLE_FP32 = 1 };
+
+typedef struct {
+    double lr, beta1, beta2, eps, weight_decay;
+    int64_t step; /* t >= 1: the number of this update, counted from 1 */
+} oracle_hparams;
+
+/* ---- bf16 <-> fp32 ---------------------------------------------------- */
+
+static double bf16_value(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16; /* bf16 is the high half of an fp32 */
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/*
+ * Nearest-even rounding of an fp32 to bf16: keep the high 16 bits, then
+ * look at the 16 dropped bits.  Above half an ulp: round up.  Exactly half:
+ * round up only if the kept pattern is odd.  Rounding up is +1 on the
+ * 16-bit pattern; a carry out of the significand moves into the exponent,
+ * which is the right result (and turns the largest finite value into inf).
+ */
+uint16_t oracle_bf16_round(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    uint16_t hi = (uint16_t)(u >> 16);
+    uint32_t dropped = u & 0xFFFFu;
+    int is_nan = ((u & 0x7F800000u) == 0x7F800000u) && (u & 0x007FFFFFu);
+    if (is_nan)
+        return (uint16_t)(hi | 0x0040u);
+    if (dropped > 0x8000u || (dropped == 0x8000u && (hi & 1u)))
+        hi = (uint16_t)(hi + 1u);
+    return hi;
+}
+
+void oracle_bf16_round_array(const float *in, int64_t n, uint16_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_round(in[i]);
+}
+
+/* ---- the three steps, per element ------------------------------------- */
+
+static double partial_at(const void *p, int gdt, int64_t i)
+{
+    if (gdt == ORACLE_BF16)
+        return bf16_value(((const uint16_t *)p)[i]);
+    return (double)((const float *)p)[i];
+}
+
+static float reduce_one(const void *const *partials, int n_ranks, int gdt, int64_t i)
+{
+    double s = partial_at(partials[0], gdt, i);
+    for (int k = 1; k < n_ranks; ++k)
+        s = s + partial_at(partials[k], gdt, i);
+    return (float)(s / (double)n_ranks);
+}
+
+static void adamw_one(float g32, float *theta, float *m, float *v, const oracle_hparams *hp,
+                      double bc1, double bc2)
+{
+    double g = g32;
+    double m1 = hp->beta1 * (double)*m + (1.0 - hp->beta1) * g;
+    double v1 = hp->beta2 * (double)*v + (1.0 - hp->beta2) * (g * g);
+    double mhat = m1 / bc1;
+    double vhat = v1 / bc2;
+    double upd = mhat / (sqrt(vhat) + hp->eps);
+    double th = (double)*theta * (1.0 - hp->lr * hp->weight_decay) - hp->lr * upd;
+    *m = (float)m1;
+    *v = (float)v1;
+    *theta = (float)th;
+}
+
+static double bias_correction(double beta, int64_t t)
+{
+    return 1.0 - pow(beta, (double)t);
+}
+
+/* ---- array entry points --------------------------------------------- */
+
+/* g_out[i] = fp32( (p_0[i] + p_1[i] + ... + p_{N-1}[i]) / N ), i in [0, n). */
+void oracle_reduce(const void *const *partials, int n_ranks, int gdt, int64_t n, float *g_out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        g_out[i] = reduce_one(partials, n_ranks, gdt, i);
+}
+
+/* One AdamW update of n elements in place, from an fp32 gradient. */
+void oracle_adamw(const float *g, float *master, float *m, float *v, int64_t n,
+                  const oracle_hparams *hp)
+{
+    double bc1 = bias_correction(hp->beta1, hp->step);
+    double bc2 = bias_correction(hp->beta2, hp->step);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        adamw_one(g[i], &master[i], &m[i], &v[i], hp, bc1, bc2);
+}
+
+/* The whole shard step: reduce, AdamW, bf16 parameter (in shard order). */
+void oracle_shard_step(const void *const *partials, int n_ranks, int gdt, int64_t n,
+                       float *master, float *m, float *v, const oracle_hparams *hp,
+                       uint16_t *param_out)
+{
+    double bc1 = bias_correction(hp->beta1, hp->step);
+    double bc2 = bias_correction(hp->beta2, hp->step);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float g = reduce_one(partials, n_ranks, gdt, i);
+        adamw_one(g, &master[i], &m[i], &v[i], hp, bc1, bc2);
+        if (param_out)
+            param_out[i] = oracle_bf16_round(master[i]);
+    }
+}
+
+/*
+ * Shard geometry: the pieces of rank `rank`'s segment, one per tensor it
+ * touches.  seg[4*j + 0..3] = {tensor id, element offset inside the tensor,
+ * offset inside the shard, length}.  Returns the number of pieces (at most
+ * cap are written) and stores the shard length S in *shard_len.
+ */
+int64_t oracle_shard_segments(const int64_t *numels, int n_tensors, int n_ranks, int rank,
+                              int64_t *seg, int64_t cap, int64_t *shard_len)
+{
+    int64_t total = 0;
+    for (int t = 0; t < n_tensors; ++t)
+        total += numels[t];
+    int64_t S = (total + n_ranks - 1) / n_ranks;
+    int64_t lo = (int64_t)rank * S, hi = lo + S;
+    if (lo > total) lo = total;
+    if (hi > total) hi = total;
+    *shard_len = S;
+    int64_t count = 0, start = 0;
+    for (int t = 0; t < n_tensors; ++t) {
+        int64_t a = start, b = start + numels[t];
+        int64_t x = a > lo ? a : lo, y = b < hi ? b : hi;
+        if (x < y) {
+            if (count < cap) {
+                seg[4 * count + 0] = t;
+                seg[4 * count + 1] = x - a;
+                seg[4 * count + 2] = x - lo;
+                seg[4 * count + 3] = y - x;
+            }
+            ++count;
+        }
+        start = b;
+    }
+    return count;
+}
+
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,88 @@
+"""The oracle's pins must reject plausible mistakes.
+
+Each case below plants one mistake in a private copy of the oracle's C
+source (on the CPU, in a temporary directory), builds it, points the oracle
+module at the broken build, and runs the fast pins.  At least one pin has
+to fail for every mutant; the real build is restored afterwards.
+"""
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+MUTANTS = {
+    "drop_last_rank": ("for (int k = 1; k < n_ranks; ++k)", "for (int k = 1; k < n_ranks - 1; ++k)"),
+    "divide_by_n_minus_1": ("(float)(s / (double)n_ranks)", "(float)(s / (double)(n_ranks > 1 ? n_ranks - 1 : 1))"),
+    "sum_not_mean": ("(float)(s / (double)n_ranks)", "(float)s"),
+    "wrong_partial_index": ("return bf16_value(((const uint16_t *)p)[i]);",
+                            "return bf16_value(((const uint16_t *)p)[i ^ 1]);"),
+    "m_weight_swapped": ("hp->beta1 * (double)*m + (1.0 - hp->beta1) * g",
+                         "(1.0 - hp->beta1) * (double)*m + hp->beta1 * g"),
+    "v_uses_beta1": ("hp->beta2 * (double)*v + (1.0 - hp->beta2) * (g * g)",
+                     "hp->beta1 * (double)*v + (1.0 - hp->beta1) * (g * g)"),
+    "v_not_squared": ("(1.0 - hp->beta2) * (g * g)", "(1.0 - hp->beta2) * fabs(g)"),
+    "no_bias_correction": ("double mhat = m1 / bc1;", "double mhat = m1;"),
+    "no_v_bias_correction": ("double vhat = v1 / bc2;", "double vhat = v1;"),
+    "eps_inside_sqrt": ("sqrt(vhat) + hp->eps", "sqrt(vhat + hp->eps)"),
+    "decay_not_scaled_by_lr": ("(1.0 - hp->lr * hp->weight_decay)", "(1.0 - hp->weight_decay)"),
+    "decay_dropped": ("(1.0 - hp->lr * hp->weight_decay)", "1.0"),
+    "update_sign": ("- hp->lr * upd", "+ hp->lr * upd"),
+    "step_off_by_one": ("pow(beta, (double)t)", "pow(beta, (double)(t - 1))"),
+    "stale_m_used": ("double mhat = m1 / bc1;", "double mhat = (double)*m / bc1;"),
+    "bf16_ties_away": ("(dropped == 0x8000u && (hi & 1u))", "(dropped == 0x8000u)"),
+    "bf16_truncate": ("hi = (uint16_t)(hi + 1u);", "hi = hi;"),
+    "shard_len_floor": ("int64_t S = (total + n_ranks - 1) / n_ranks;", "int64_t S = total / n_ranks;"),
+    "segment_offset": ("seg[4 * count + 1] = x - a;", "seg[4 * count + 1] = x - lo;"),
+}
+
+FAST_PINS = [
+    lambda: pins.test_bf16_round_special_values(),
+    lambda: pins.test_reduce_equals_exact_rational_mean(3),
+    lambda: pins.test_reduce_equals_exact_rational_mean(8),
+    lambda: pins.test_gradient_averaging_identity_linear_model("f32"),
+    lambda: pins.test_allreduce_equals_reduce_scatter_plus_all_gather(),
+    lambda: pins.test_adamw_matches_torch_adamw_float64(pins.HP_VARIANTS[0]),
+    lambda: pins.test_adamw_step1_closed_form(),
+    lambda: pins.test_adamw_zero_gradient_decay_only(),
+    lambda: pins.test_adamw_zero_betas_reduce_to_normalised_step(),
+    lambda: pins.test_adamw_constant_gradient_unbiased_moments(),
+    lambda: [pins.test_shard_segments_brute_force(s) for s in range(6)],
+]
+
+
+def _failing_pins():
+    failed = 0
+    for pin in FAST_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    return failed
+
+
+def test_real_oracle_passes_fast_pins():
+    assert _failing_pins() == 0
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    src = open(oracle.SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "mutant.c")
+        so = os.path.join(d, "libmutant.so")
+        open(c, "w").write(src.replace(old, new))
+        subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC",
+                        "-shared", "-w", "-o", so, c, "-lm"], check=True)
+        oracle.use_library(so)
+        try:
+            failed = _failing_pins()
+        finally:
+            oracle.use_library(None)
+    assert failed >= 1, f"no pin caught mutant {name}"
