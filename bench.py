@@ -1,0 +1,298 @@
+"""Benchmark of the fused ZeRO shard step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama7b]
+
+A step is one call of zero_shard_step: reduce the N gradient partials of
+this rank's shard, AdamW on the shard's fp32 master/m/v, write the bf16
+parameters into their slots.  Inputs are synthetic, seeded, and resident
+in HBM before timing starts.  The partials are the same for every timed
+step (one batch); the optimizer state advances.
+
+Prints one JSON line: params/s over the shard, the roofline block of the
+step kernel (algorithmic HBM bytes per launch / measured launch time against
+the 8 TB/s HBM peak), and the CPU oracle timed on a bounded sample of the
+same workload on this host.
+
+The workload setup below (allocation, device fill, warm start) is also what
+the full-size GPU parity tests run, so they check the configuration timed
+here.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from synth import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+KERNEL_SOURCES = [os.path.join(ROOT, "sharded_optimizer_step_shard_amd", "csrc", f)
+                  for f in ("zero_kernels.hip", "zero_api.cpp", "zero_internal.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def default_dst_mode(w: W.Workload) -> str:
+    # The 70B full parameter buffer (141 GB) does not fit beside the partials
+    # and state; only this rank's slot is allocated there.
+    return "slot" if w.name == "llama-70b" else "tensors"
+
+
+class Shard:
+    """Device buffers of one rank's shard step for a workload."""
+
+    def __init__(self, w: W.Workload, rank: int = 0, dst_mode: str = None,
+                 max_chunk: int = 65536, device: str = "cuda"):
+        import torch
+        import sharded_optimizer_step_shard_amd as zs
+
+        self.w, self.rank, self.zs = w, rank, zs
+        self.dst_mode = dst_mode or default_dst_mode(w)
+        self.lo, self.hi = w.shard_range(rank)
+        self.n = self.hi - self.lo
+        self.S = w.shard_len
+        dev = torch.device(device)
+        self.dev = dev
+        gtype = torch.int16 if w.gdt == "bf16" else torch.float32
+        self.partials = [torch.empty(self.n, dtype=gtype, device=dev) for _ in range(w.n_ranks)]
+        self.master = torch.empty(self.n, dtype=torch.float32, device=dev)
+        self.m = torch.zeros(self.n, dtype=torch.float32, device=dev)
+        self.v = torch.zeros(self.n, dtype=torch.float32, device=dev)
+        if self.dst_mode == "slot":
+            self.params = [torch.zeros(self.n, dtype=torch.int16, device=dev)]
+            table, S = zs.zero_build_chunks(w.numels, w.n_ranks, rank, slot_dst=self.params[0],
+                                            max_chunk=max_chunk)
+        elif self.dst_mode == "tensors":
+            self.params = [torch.zeros(k, dtype=torch.int16, device=dev) for k in w.numels]
+            table, S = zs.zero_build_chunks(w.numels, w.n_ranks, rank, tensor_dst=self.params,
+                                            max_chunk=max_chunk)
+        else:
+            raise ValueError(self.dst_mode)
+        assert S == self.S
+        self.table = table
+        self.d_table = zs.chunks_to_device(table, dev)
+        self.step_t = 0
+        synth.dev_fill(self.master, w.seed, synth.stream_id(synth.KIND_MASTER), self.lo,
+                       w.sigma_master)
+
+    # -- inputs -------------------------------------------------------------
+    def grad_stream(self, k: int, t: int) -> int:
+        return synth.stream_id(synth.KIND_GRAD, k, t)
+
+    def mask_stream(self, k: int, t: int) -> int:
+        return synth.stream_id(synth.KIND_OUTLIER, k, t)
+
+    def fill_partials(self, t: int, count: int = None) -> None:
+        """Partials of gradient step t (per rank k: stream (grad, k, t) at the
+        global flat indices of this shard); zero tensors zeroed."""
+        w = self.w
+        for k, p in enumerate(self.partials):
+            dst = p if count is None else p[:count]
+            synth.dev_fill(dst, w.seed, self.grad_stream(k, t), self.lo, w.sigma_grad,
+                           self.mask_stream(k, t), w.outlier_frac, w.outlier_mult)
+            for a, b in W.zero_ranges(w, self.lo, self.hi):
+                if count is not None:
+                    b = min(b, count)
+                if a < b:
+                    dst[a:b].zero_()
+
+    def warm_start(self) -> None:
+        """m, v warm start: warm_steps steps on the first warm_prefix shard
+        elements (fresh partials each step), then every later element takes
+        m, v from prefix element src(i) = hash(i) mod warm_prefix."""
+        import torch
+        w = self.w
+        P = w.warm_prefix
+        assert 0 < P <= self.n and P % 64 == 0
+        # Prefix steps write their bf16 parameters into a scratch slot.
+        scratch = torch.empty(P, dtype=torch.int16, device=self.dev)
+        table, _ = self.zs.zero_build_chunks([P], 1, 0, slot_dst=scratch, max_chunk=4096)
+        d_table = self.zs.chunks_to_device(table, self.dev)
+        for t in range(1, w.warm_steps + 1):
+            self.fill_partials(t, count=P)
+            self.zs.zero_shard_step([p[:P] for p in self.partials], self.master[:P], self.m[:P],
+                                    self.v[:P], P, d_table, len(table),
+                                    self.zs.hparams(t, **w.hparams()))
+        mp, vp = self.m[:P].clone(), self.v[:P].clone()
+        st = synth.stream_id(synth.KIND_PREFIX_MAP)
+        synth.dev_spread(self.m, mp, w.seed, st, 0)
+        synth.dev_spread(self.v, vp, w.seed, st, 0)
+        torch.cuda.synchronize()
+        self.step_t = w.warm_steps
+
+    def prepare(self) -> int:
+        """Bench inputs: warm start if the workload has one, then the partials
+        of the first timed step.  Returns that step number."""
+        if self.w.warm_prefix:
+            self.warm_start()
+        t0 = self.step_t + 1
+        self.fill_partials(t0)
+        return t0
+
+    # -- the step -------------------------------------------------------------
+    def step(self, t: int) -> None:
+        self.zs.zero_shard_step(self.partials, self.master, self.m, self.v, self.n,
+                                self.d_table, len(self.table),
+                                self.zs.hparams(t, **self.w.hparams()))
+        self.step_t = t
+
+    def param_at(self, shard_idx: np.ndarray):
+        """bf16 bits written for the given shard indices (device gather)."""
+        import torch
+        if self.dst_mode == "slot":
+            flat = self.params[0]
+            idx = torch.from_numpy(shard_idx).to(self.dev)
+            return flat[idx].cpu().numpy().view(np.uint16)
+        starts = np.cumsum([0] + self.w.numels[:-1])
+        g = shard_idx + self.lo
+        t = np.searchsorted(starts, g, side="right") - 1
+        out = np.empty(len(g), np.uint16)
+        for tt in np.unique(t):
+            sel = np.nonzero(t == tt)[0]
+            idx = torch.from_numpy(g[sel] - starts[tt]).to(self.dev)
+            out[sel] = self.params[tt][idx].cpu().numpy().view(np.uint16)
+        return out
+
+    def bytes_per_launch(self) -> int:
+        return self.w.bytes_per_param() * self.n
+
+
+def cpu_baseline(w: W.Workload, rank: int, t: int, target_s: float = 10.0,
+                 sample: int = 1 << 22) -> dict:
+    """The CPU oracle on a bounded sample (the first `sample` shard elements)
+    of the same workload, repeated until ~target_s of work; params/s."""
+    import oracle
+
+    lo, hi = w.shard_range(rank)
+    n = min(sample, hi - lo)
+    parts = [synth.fill(w.gdt, w.seed, synth.stream_id(synth.KIND_GRAD, k, t), lo, n,
+                        w.sigma_grad, synth.stream_id(synth.KIND_OUTLIER, k, t),
+                        w.outlier_frac, w.outlier_mult) for k in range(w.n_ranks)]
+    master = synth.fill("f32", w.seed, synth.stream_id(synth.KIND_MASTER), lo, n, w.sigma_master)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    done, elapsed, reps = 0, 0.0, 0
+    while elapsed < target_s:
+        t0 = time.perf_counter()
+        oracle.shard_step(parts, master, m, v, oracle.hparams(t + reps, **w.hparams()),
+                          in_place=True)
+        elapsed += time.perf_counter() - t0
+        done += n
+        reps += 1
+    return {"value": done / elapsed, "unit": "params/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"first {n} elements of rank {rank}'s shard of {w.name}, N={w.n_ranks} "
+                      f"{w.gdt} partials, {reps} oracle steps in {elapsed:.1f} s"}
+
+
+def load_traffic(kernel_key: str) -> dict:
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE)).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b", choices=sorted(W.ALL))
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--dst", default=None, choices=["slot", "tensors"])
+    ap.add_argument("--max-chunk", type=int, default=65536)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs one rank's shard step on one GPU; "
+                                   "--gpus above 1 is not supported (the collectives that "
+                                   "would feed it are out of scope)"}), flush=True)
+        return 2
+
+    import torch
+
+    w = W.get(args.workload)
+    sh = Shard(w, args.rank, args.dst, args.max_chunk)
+    t = sh.prepare()
+    torch.cuda.synchronize()
+    print(f"# {w.name}: shard {sh.n} params, N={w.n_ranks} {w.gdt}, {len(sh.table)} chunks, "
+          f"dst={sh.dst_mode}, first timed step t={t + args.warmup}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        sh.step(t)
+        t += 1
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        sh.step(t)
+        t += 1
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps   # one launch per step
+    ms_per_step = wall * 1e3 / args.steps
+
+    bytes_launch = sh.bytes_per_launch()
+    achieved = bytes_launch / (kernel_ms * 1e-3) / 1e9
+    kernel_key = f"shard_step_kernel<{w.gdt},{w.n_ranks}>/{w.name}"
+    traffic = load_traffic(kernel_key)
+    out = {
+        "metric": "params updated/sec and achieved HBM GB/s (fraction of peak), fused shard step",
+        "value": sh.n / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} rank-{args.rank} shard", "shard_params": sh.n,
+                   "n_ranks": w.n_ranks, "grad_dtype": w.gdt, "state_dtype": "fp32",
+                   "param_dtype": "bf16", "tensors": len(w.numels), "chunks": len(sh.table),
+                   "dst": sh.dst_mode, "bytes_per_param": w.bytes_per_param(),
+                   "parallelism": "one data-parallel rank's ZeRO shard"},
+        "hbm_gbs": achieved,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                     "kernel": kernel_key, "kernel_ms": kernel_ms,
+                     "algorithmic_bytes_per_launch": bytes_launch},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.rank, t, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

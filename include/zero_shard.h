@@ -1,0 +1,208 @@
+/*
+ * zero_shard.h -- C ABI of the ZeRO/FSDP per-rank optimizer-step library
+ * for AMD Instinct MI355X (gfx950).  Library: libzero_shard.so.
+ *
+ * One data-parallel rank owns a contiguous segment ("shard") of the flat
+ * parameter vector.  Its optimizer step has three parts:
+ *
+ *   1. reduce    g[i] = (p_0[i] + ... + p_{N-1}[i]) / N over the N ranks'
+ *                gradient partials for this shard: the local arithmetic of
+ *                the gradient reduce-scatter ("CS336 2026 Lecture 8:
+ *                Parallelism Basics", Slide 8: all-reduce = reduce-scatter +
+ *                all-gather; "并行策略总览：六个维度各切什么、怎么通信", data-parallel
+ *                section: the full-batch gradient is the mean of the ranks'
+ *                gradients).
+ *   2. AdamW     on the shard's fp32 master weights and Adam moments m, v,
+ *                which only this rank keeps (Lecture 8, Slides 17 and 19-20:
+ *                the 16-bytes-per-parameter ledger, optimizer state sharded).
+ *   3. write     the updated parameters, rounded to bf16, into this rank's
+ *                slot of the full parameter buffer: the local half of the
+ *                parameter all-gather (Lecture 8, Slide 20, fourth step;
+ *                "并行训练优化、MoE扩展与系统瓶颈", 2.2.1 and 2.2.4).
+ *
+ * zero_shard_step does all three in one pass over HBM; zero_reduce_shard,
+ * zero_adamw_shard and zero_gather_write do them one at a time and give the
+ * same bits.
+ *
+ * Arithmetic, fixed so that every result is reproducible bit for bit:
+ *   - g: the partials are widened exactly to double and summed in double,
+ *     rank 0 first, ranks 1..N-1 in order; the sum is divided by N in
+ *     double and rounded once to fp32 (the reduced gradient shard is an
+ *     fp32 tensor).
+ *   - AdamW (decoupled weight decay, bias correction, eps outside the root),
+ *     every operation an IEEE double operation without fused multiply-add:
+ *         m' = b1 m + (1 - b1) g
+ *         v' = b2 v + (1 - b2) (g g)
+ *         theta' = theta (1 - lr wd) - lr (m'/(1 - b1^t)) / (sqrt(v'/(1 - b2^t)) + eps)
+ *     m', v', theta' rounded once to fp32.  (1 - b1), (1 - b2), (1 - lr wd)
+ *     and b^t = pow(b, t) are formed in double.
+ *   - the bf16 parameter is theta' (fp32) rounded to nearest even; NaN
+ *     stays NaN with its sign and the quiet bit set; overflow gives inf.
+ *   Non-finite inputs propagate per IEEE; there is no clipping or skipping.
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are device pointers unless stated otherwise.
+ *     The caller owns all memory.  The library never allocates or frees
+ *     device memory and keeps no global mutable state; calls are re-entrant.
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call
+ *     returns without synchronising.  Device faults surface at the caller's
+ *     next synchronisation, as usual for HIP.
+ *   - Every check runs on the host before anything is launched; a call that
+ *     returns an error has launched nothing and changed nothing.  Checks,
+ *     in order: null pointers and counts (INVALID), 16-byte alignment
+ *     (MISALIGNED), dtype (UNSUPPORTED), overlap of inputs with outputs
+ *     (ALIAS), and finally that every array range lies inside one device
+ *     allocation (NOT_DEVICE, via hipMemGetAddressRange).  The chunk
+ *     table's dst addresses live in device memory and are not checked: they
+ *     must come from zero_build_chunks over live parameter buffers.
+ *   - Base pointers of partials, state arrays and grad arrays must be 16-byte
+ *     aligned (torch allocations are).  Lengths and offsets are arbitrary.
+ *   - When the element count is 0 the call does nothing and its array
+ *     pointers may be NULL (an empty shard).
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of the gradient partials. */
+typedef enum zero_dtype {
+    ZERO_BF16 = 0,   /* bfloat16, passed as 16-bit patterns */
+    ZERO_FP32 = 1    /* IEEE binary32 (the pages' fp32-gradient communication case) */
+} zero_dtype;
+
+/* AdamW hyper-parameters, in double.  `step` is t >= 1, the number of this
+ * update counted from 1 (bias corrections use b1^t and b2^t).
+ * Requirements: finite lr, eps, weight_decay; 0 <= beta1, beta2 < 1. */
+typedef struct zero_adamw_hparams {
+    double lr;
+    double beta1;
+    double beta2;
+    double eps;
+    double weight_decay;
+    int64_t step;
+} zero_adamw_hparams;
+
+/* One chunk of a shard: shard elements [shard_off, shard_off + len), whose
+ * bf16 parameters go to dst[0 .. len).  32 bytes.  Built on the host by
+ * zero_build_chunks; the caller copies the table to device memory. */
+typedef struct zero_chunk {
+    int64_t shard_off;   /* first shard element of the chunk */
+    uint16_t *dst;       /* device address of the bf16 parameter of shard_off */
+    int32_t len;         /* element count, 1 .. max_chunk */
+    int32_t tensor_id;   /* tensor holding shard element shard_off */
+    int64_t tensor_off;  /* element offset of shard_off inside that tensor */
+} zero_chunk;
+
+/* Return codes. */
+enum {
+    ZERO_OK = 0,
+    ZERO_ERR_INVALID = 1,      /* null pointer, bad count or length, bad hyper-parameter */
+    ZERO_ERR_MISALIGNED = 2,   /* a base pointer is not 16-byte aligned */
+    ZERO_ERR_UNSUPPORTED = 3,  /* unknown dtype */
+    ZERO_ERR_ALIAS = 4,        /* an input array overlaps an array the call writes */
+    ZERO_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
+    ZERO_ERR_CAPACITY = 6,     /* caller's chunk array too small (see n_out) */
+    ZERO_ERR_NOT_DEVICE = 7    /* an array is not inside one device allocation */
+};
+
+#define ZERO_MAX_RANKS 64
+#define ZERO_DEFAULT_MAX_CHUNK 65536
+
+/*
+ * Shard geometry and the chunk table (host only; no device calls).
+ *
+ * The parameters are the n_tensors tensors concatenated in order (numels[t]
+ * elements each, host array), total T.  With n_ranks ranks the shard length
+ * is S = ceil(T / n_ranks) and rank `rank` owns flat elements
+ * [rank*S, min((rank+1)*S, T)) -- contiguous, cutting across tensor
+ * boundaries; the last shards may be shorter or empty (Lecture 8,
+ * Slides 19-20: each rank updates one segment of the parameters).
+ *
+ * Destination of the bf16 parameters, one of:
+ *   tensor_dst != NULL: host array of n_tensors device pointers; element e
+ *     of tensor t is written to tensor_dst[t] + e.  Chunks never cross a
+ *     tensor boundary.
+ *   tensor_dst == NULL: slot_dst is the device address of this rank's slot
+ *     (for a flat full parameter buffer P, slot_dst = P + rank*S); shard
+ *     element i is written to slot_dst + i.  Chunks may cross tensors.
+ * Chunks are also cut every max_chunk elements of the shard (max_chunk a
+ * positive multiple of 64, at most 2^24).
+ *
+ * out: host array of cap chunks, or NULL to query the count only.
+ * *n_out receives the number of chunks needed, *shard_len_out receives the
+ * shard length S (both may be NULL).  Returns ZERO_ERR_CAPACITY if out is
+ * not NULL and cap < *n_out (nothing written beyond cap).
+ */
+int zero_build_chunks(const int64_t *numels, int n_tensors, int n_ranks, int rank,
+                      uint16_t *const *tensor_dst, uint16_t *slot_dst, int64_t max_chunk,
+                      zero_chunk *out, int64_t cap, int64_t *n_out, int64_t *shard_len_out);
+
+/*
+ * The fused shard step: reduce + AdamW + bf16 write in one pass.
+ *
+ * partials:  host array of n_ranks device pointers; partials[k] holds rank
+ *            k's gradient for this shard, shard_len elements of type gdt,
+ *            read only.  1 <= n_ranks <= ZERO_MAX_RANKS.
+ * master, m, v: fp32 device arrays of shard_len elements, updated in place.
+ * d_chunks, n_chunks: the chunk table in device memory (from
+ *            zero_build_chunks for this shard_len); chunks outside
+ *            [0, shard_len) are skipped.  Shard elements no chunk covers
+ *            are left untouched.
+ * hp:        host pointer to the hyper-parameters of this step.
+ * Errors: INVALID (null, n_ranks out of range, shard_len < 0, n_chunks < 0,
+ * bad hp), MISALIGNED, UNSUPPORTED (gdt), NOT_DEVICE, ALIAS (a partial overlaps master,
+ * m or v, or those overlap each other), HIP.
+ */
+int zero_shard_step(const void *const *partials, int n_ranks, zero_dtype gdt,
+                    float *master, float *m, float *v, int64_t shard_len,
+                    const zero_chunk *d_chunks, int64_t n_chunks,
+                    const zero_adamw_hparams *hp, hipStream_t stream);
+
+/*
+ * Reduce only: grad_out[i] = fp32((p_0[i] + ... + p_{N-1}[i]) / N),
+ * i in [0, n), summed in double in rank order.  grad_out must not overlap
+ * any partial (ALIAS).  n == 0 is a no-op.
+ */
+int zero_reduce_shard(const void *const *partials, int n_ranks, zero_dtype gdt, int64_t n,
+                      float *grad_out, hipStream_t stream);
+
+/*
+ * AdamW only, from an fp32 gradient: master, m, v (n elements each) are
+ * updated in place exactly as in zero_shard_step.  grad must not overlap
+ * master, m or v (ALIAS).  n == 0 is a no-op.
+ */
+int zero_adamw_shard(const float *grad, float *master, float *m, float *v, int64_t n,
+                     const zero_adamw_hparams *hp, hipStream_t stream);
+
+/*
+ * bf16 write only: for every chunk c and j < c.len,
+ * c.dst[j] = bf16(master[c.shard_off + j]).  master holds shard_len fp32
+ * elements; chunks outside [0, shard_len) are skipped.
+ */
+int zero_gather_write(const float *master, int64_t shard_len, const zero_chunk *d_chunks,
+                      int64_t n_chunks, hipStream_t stream);
+
+/* Static description of a return code. */
+const char *zero_strerror(int code);
+
+/* Library version, (major << 16) | minor. */
+int zero_version(void);
+
+/*
+ * Measurement aid, not part of the step: copies `bytes` bytes from src to
+ * dst (device, 16-byte aligned, non-overlapping) with a streaming kernel.
+ * Used to calibrate HBM traffic counters and the attainable copy bandwidth.
+ */
+int zero_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_SHARD_H */

@@ -1,0 +1,201 @@
+"""Python binding of libzero_shard.so, the MI355X ZeRO shard-step library.
+
+Same names as the C ABI in include/zero_shard.h.  This module only marshals
+arguments (torch tensors or raw device addresses -> pointers, the current
+torch stream -> hipStream_t) and turns non-zero return codes into
+exceptions.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback.  If the library has not been built, importing
+this package raises.
+
+    import sharded_optimizer_step_shard_amd as zs
+    table, S = zs.zero_build_chunks(numels, n_ranks, rank, slot_dst=slot_ptr)
+    d_table = zs.chunks_to_device(table)
+    zs.zero_shard_step(partials, master, m, v, S, d_table, len(table), hp)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libzero_shard.so")
+
+ZERO_BF16, ZERO_FP32 = 0, 1
+ZERO_OK, ZERO_ERR_INVALID, ZERO_ERR_MISALIGNED, ZERO_ERR_UNSUPPORTED = 0, 1, 2, 3
+ZERO_ERR_ALIAS, ZERO_ERR_HIP, ZERO_ERR_CAPACITY, ZERO_ERR_NOT_DEVICE = 4, 5, 6, 7
+ZERO_MAX_RANKS = 64
+ZERO_DEFAULT_MAX_CHUNK = 65536
+
+# Mirrors `zero_chunk` (32 bytes).
+CHUNK_DTYPE = np.dtype([("shard_off", "<i8"), ("dst", "<u8"), ("len", "<i4"),
+                        ("tensor_id", "<i4"), ("tensor_off", "<i8")], align=True)
+assert CHUNK_DTYPE.itemsize == 32
+
+
+class HParams(ctypes.Structure):
+    """Mirrors `zero_adamw_hparams`."""
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64)]
+
+
+def hparams(step: int, lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999,
+            eps: float = 1e-8, weight_decay: float = 0.1) -> HParams:
+    return HParams(lr, beta1, beta2, eps, weight_decay, step)
+
+
+class ZeroShardError(RuntimeError):
+    def __init__(self, code: int, fn: str):
+        self.code = code
+        super().__init__(f"{fn} failed: {code} ({zero_strerror(code)})")
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first "
+                      "(python -m sharded_optimizer_step_shard_amd.build)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+_lib.zero_build_chunks.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp, _i64,
+                                   ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+_lib.zero_shard_step.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64,
+                                 ctypes.POINTER(HParams), _vp]
+_lib.zero_reduce_shard.argtypes = [_vp, _i32, _i32, _i64, _vp, _vp]
+_lib.zero_adamw_shard.argtypes = [_vp, _vp, _vp, _vp, _i64, ctypes.POINTER(HParams), _vp]
+_lib.zero_gather_write.argtypes = [_vp, _i64, _vp, _i64, _vp]
+_lib.zero_probe_copy.argtypes = [_vp, _vp, _i64, _vp]
+_lib.zero_strerror.argtypes = [_i32]
+_lib.zero_strerror.restype = ctypes.c_char_p
+for _f in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
+           "zero_gather_write", "zero_probe_copy", "zero_version"):
+    getattr(_lib, _f).restype = _i32
+
+Ptr = Union[int, "torch.Tensor", None]  # noqa: F821
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _addr(x: Ptr) -> Optional[int]:
+    """Device address of a tensor (must be contiguous and on a GPU) or a raw int."""
+    if x is None:
+        return None
+    if isinstance(x, (int, np.integer)):
+        return int(x)
+    if not x.is_cuda:
+        raise ValueError("tensor arguments must live in device memory")
+    if not x.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _gdt_of(partials) -> int:
+    p0 = partials[0]
+    if isinstance(p0, (int, np.integer)):
+        raise ValueError("pass gdt explicitly with raw partial addresses")
+    import torch
+    if p0.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return ZERO_BF16
+    if p0.dtype == torch.float32:
+        return ZERO_FP32
+    raise ValueError(f"unsupported partial dtype {p0.dtype}")
+
+
+def _check(code: int, fn: str) -> None:
+    if code != ZERO_OK:
+        raise ZeroShardError(code, fn)
+
+
+def zero_strerror(code: int) -> str:
+    return _lib.zero_strerror(code).decode()
+
+
+def zero_version() -> Tuple[int, int]:
+    v = _lib.zero_version()
+    return v >> 16, v & 0xFFFF
+
+
+def zero_build_chunks(numels: Sequence[int], n_ranks: int, rank: int,
+                      tensor_dst: Optional[Sequence[Ptr]] = None, slot_dst: Ptr = None,
+                      max_chunk: int = ZERO_DEFAULT_MAX_CHUNK) -> Tuple[np.ndarray, int]:
+    """Host chunk table (numpy array of CHUNK_DTYPE) and the shard length S."""
+    nm = np.ascontiguousarray(numels, dtype=np.int64)
+    td = None
+    if tensor_dst is not None:
+        td = (ctypes.c_void_p * len(tensor_dst))(*[_addr(t) for t in tensor_dst])
+    n = _i64(0)
+    S = _i64(0)
+    _check(_lib.zero_build_chunks(nm.ctypes.data, len(nm), n_ranks, rank, td, _addr(slot_dst),
+                                  max_chunk, None, 0, ctypes.byref(n), ctypes.byref(S)),
+           "zero_build_chunks")
+    out = np.zeros(n.value, dtype=CHUNK_DTYPE)
+    if n.value:
+        _check(_lib.zero_build_chunks(nm.ctypes.data, len(nm), n_ranks, rank, td,
+                                      _addr(slot_dst), max_chunk, out.ctypes.data, n.value,
+                                      ctypes.byref(n), ctypes.byref(S)), "zero_build_chunks")
+    return out, S.value
+
+
+def chunks_to_device(table: np.ndarray, device: str = "cuda"):
+    """Copy a host chunk table into a device buffer (torch owns the memory)."""
+    import torch
+    raw = torch.from_numpy(np.ascontiguousarray(table).view(np.uint8).copy())
+    return raw.to(device)
+
+
+def _partial_array(partials):
+    addrs = [_addr(p) for p in partials]
+    return (ctypes.c_void_p * max(len(addrs), 1))(*addrs)
+
+
+def zero_shard_step(partials: Sequence[Ptr], master: Ptr, m: Ptr, v: Ptr, shard_len: int,
+                    d_chunks: Ptr, n_chunks: int, hp: HParams, gdt: Optional[int] = None,
+                    stream=None) -> None:
+    """Fused reduce + AdamW + bf16 write of one shard (asynchronous on `stream`)."""
+    gdt = _gdt_of(partials) if gdt is None else gdt
+    _check(_lib.zero_shard_step(_partial_array(partials), len(partials), gdt, _addr(master),
+                                _addr(m), _addr(v), shard_len, _addr(d_chunks), n_chunks,
+                                ctypes.byref(hp), _stream(stream)), "zero_shard_step")
+
+
+def zero_reduce_shard(partials: Sequence[Ptr], n: int, grad_out: Ptr,
+                      gdt: Optional[int] = None, stream=None) -> None:
+    gdt = _gdt_of(partials) if gdt is None else gdt
+    _check(_lib.zero_reduce_shard(_partial_array(partials), len(partials), gdt, n,
+                                  _addr(grad_out), _stream(stream)), "zero_reduce_shard")
+
+
+def zero_adamw_shard(grad: Ptr, master: Ptr, m: Ptr, v: Ptr, n: int, hp: HParams,
+                     stream=None) -> None:
+    _check(_lib.zero_adamw_shard(_addr(grad), _addr(master), _addr(m), _addr(v), n,
+                                 ctypes.byref(hp), _stream(stream)), "zero_adamw_shard")
+
+
+def zero_gather_write(master: Ptr, shard_len: int, d_chunks: Ptr, n_chunks: int,
+                      stream=None) -> None:
+    _check(_lib.zero_gather_write(_addr(master), shard_len, _addr(d_chunks), n_chunks,
+                                  _stream(stream)), "zero_gather_write")
+
+
+def zero_probe_copy(src: Ptr, dst: Ptr, nbytes: int, stream=None) -> None:
+    _check(_lib.zero_probe_copy(_addr(src), _addr(dst), nbytes, _stream(stream)),
+           "zero_probe_copy")
+
+
+def raw_call(name: str, *args) -> int:
+    """Call a C entry point with raw ctypes arguments and return its code
+    (used by the boundary tests to reach the error paths directly)."""
+    return getattr(_lib, name)(*args)

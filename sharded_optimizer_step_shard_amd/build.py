@@ -1,0 +1,51 @@
+"""Build libzero_shard.so (the HIP library behind include/zero_shard.h) in-tree.
+
+    python -m sharded_optimizer_step_shard_amd.build
+
+compiles csrc/zero_kernels.hip and csrc/zero_api.cpp for gfx950 with hipcc.
+Flags that matter for the results:
+  -ffp-contract=off  no fused multiply-add: the double arithmetic of the step
+                     must be the separately rounded operations it is defined as.
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                     keep the compiler from emitting packed fp32 instructions.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libzero_shard.so")
+ARCH = os.environ.get("ZERO_SHARD_ARCH", "gfx950")
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    return "hipcc"
+
+
+def build(verbose: bool = True, out: str = LIB, extra=()) -> str:
+    srcs = [os.path.join(CSRC, "zero_kernels.hip"), os.path.join(CSRC, "zero_api.cpp")]
+    cmd = [hipcc(), *HIP_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-o", out, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return out
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

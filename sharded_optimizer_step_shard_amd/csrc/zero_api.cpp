@@ -1,0 +1,329 @@
+// Host side of libzero_shard.so: argument checks, step constants, the chunk
+// table builder and the C entry points declared in include/zero_shard.h.
+// Nothing here allocates device memory or keeps global state.
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "zero_internal.h"
+
+using namespace zs;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// [a, a + na) and [b, b + nb) (bytes) overlap?
+bool overlaps(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    if (na <= 0 || nb <= 0)
+        return false;
+    uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+bool valid_hparams(const zero_adamw_hparams *hp)
+{
+    if (!hp || hp->step < 1)
+        return false;
+    if (!isfinite(hp->lr) || !isfinite(hp->eps) || !isfinite(hp->weight_decay))
+        return false;
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+        return false;
+    return true;
+}
+
+// Every step constant is formed here once, in double, by the same
+// operations the element-wise definition uses.
+StepScalars make_scalars(const zero_adamw_hparams *hp)
+{
+    StepScalars k;
+    k.b1 = hp->beta1;
+    k.c1 = 1.0 - hp->beta1;
+    k.b2 = hp->beta2;
+    k.c2 = 1.0 - hp->beta2;
+    k.bc1 = 1.0 - pow(hp->beta1, (double)hp->step);
+    k.bc2 = 1.0 - pow(hp->beta2, (double)hp->step);
+    k.eps = hp->eps;
+    k.lr = hp->lr;
+    k.dec = 1.0 - hp->lr * hp->weight_decay;
+    return k;
+}
+
+ReduceScalars make_reduce(int n_ranks)
+{
+    ReduceScalars r;
+    r.n_ranks = n_ranks;
+    r.n = (double)n_ranks;
+    r.pow2 = (n_ranks & (n_ranks - 1)) == 0;
+    r.inv_n = 1.0 / r.n;   // exact when n_ranks is a power of two
+    return r;
+}
+
+int elem_bytes(zero_dtype gdt) { return gdt == ZERO_BF16 ? 2 : 4; }
+
+// Shared checks of the partial list; fills pp.  With n == 0 nothing is
+// dereferenced, so null partial addresses are accepted (empty tensors).
+int check_partials(const void *const *partials, int n_ranks, zero_dtype gdt, int64_t n,
+                   PartialPtrs &pp)
+{
+    if (gdt != ZERO_BF16 && gdt != ZERO_FP32)
+        return ZERO_ERR_UNSUPPORTED;
+    if (!partials || n_ranks < 1 || n_ranks > ZERO_MAX_RANKS)
+        return ZERO_ERR_INVALID;
+    memset(&pp, 0, sizeof(pp));
+    for (int k = 0; k < n_ranks; ++k) {
+        if (!partials[k] && n > 0)
+            return ZERO_ERR_INVALID;
+        if (!aligned16(partials[k]))
+            return ZERO_ERR_MISALIGNED;
+        pp.p[k] = partials[k];
+    }
+    return ZERO_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ZERO_OK : ZERO_ERR_HIP; }
+
+// [p, p + bytes) lies inside one device allocation?  Turns a stray host or
+// freed address into an error code instead of a GPU memory fault.  A failed
+// query's error is cleared so it cannot surface at the caller's next check.
+bool in_device_alloc(const void *p, int64_t bytes)
+{
+    if (bytes <= 0)
+        return true;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return (uintptr_t)p >= (uintptr_t)base && (uintptr_t)p + (uint64_t)bytes <= (uintptr_t)base + size;
+}
+
+}  // namespace
+
+extern "C" {
+
+int zero_version(void) { return (1 << 16) | 0; }
+
+const char *zero_strerror(int code)
+{
+    switch (code) {
+    case ZERO_OK: return "ok";
+    case ZERO_ERR_INVALID: return "invalid argument";
+    case ZERO_ERR_MISALIGNED: return "base pointer not 16-byte aligned";
+    case ZERO_ERR_UNSUPPORTED: return "unsupported gradient dtype";
+    case ZERO_ERR_ALIAS: return "input overlaps an output";
+    case ZERO_ERR_HIP: return "HIP launch error";
+    case ZERO_ERR_CAPACITY: return "chunk array too small";
+    case ZERO_ERR_NOT_DEVICE: return "array not inside one device allocation";
+    default: return "unknown error code";
+    }
+}
+
+int zero_build_chunks(const int64_t *numels, int n_tensors, int n_ranks, int rank,
+                      uint16_t *const *tensor_dst, uint16_t *slot_dst, int64_t max_chunk,
+                      zero_chunk *out, int64_t cap, int64_t *n_out, int64_t *shard_len_out)
+{
+    if (!numels || n_tensors < 1 || n_ranks < 1 || rank < 0 || rank >= n_ranks)
+        return ZERO_ERR_INVALID;
+    if (max_chunk <= 0 || max_chunk % 64 != 0 || max_chunk > (int64_t(1) << 24))
+        return ZERO_ERR_INVALID;
+    if (!tensor_dst && !slot_dst)
+        return ZERO_ERR_INVALID;
+    if (out && cap < 0)
+        return ZERO_ERR_INVALID;
+    int64_t total = 0;
+    for (int t = 0; t < n_tensors; ++t) {
+        if (numels[t] < 0 || (tensor_dst && numels[t] > 0 && !tensor_dst[t]))
+            return ZERO_ERR_INVALID;
+        total += numels[t];
+    }
+    const int64_t S = (total + n_ranks - 1) / n_ranks;
+    int64_t lo = (int64_t)rank * S, hi = lo + S;
+    if (lo > total) lo = total;
+    if (hi > total) hi = total;
+
+    int64_t count = 0;
+    auto emit = [&](int64_t soff, int64_t len, int t, int64_t toff, uint16_t *dst) {
+        if (out && count < cap) {
+            zero_chunk &c = out[count];
+            c.shard_off = soff;
+            c.len = (int32_t)len;
+            c.tensor_id = t;
+            c.tensor_off = toff;
+            c.dst = dst;
+        }
+        ++count;
+    };
+    if (tensor_dst) {
+        // One piece per tensor that meets [lo, hi), each cut at multiples
+        // of max_chunk in shard coordinates.
+        int64_t a = 0;
+        for (int t = 0; t < n_tensors && a < hi; ++t) {
+            const int64_t b = a + numels[t];
+            for (int64_t x = a > lo ? a : lo, y = b < hi ? b : hi; x < y;) {
+                const int64_t soff = x - lo;
+                int64_t end = lo + (soff / max_chunk + 1) * max_chunk;
+                if (end > y) end = y;
+                emit(soff, end - x, t, x - a, tensor_dst[t] + (x - a));
+                x = end;
+            }
+            a = b;
+        }
+    } else {
+        // Contiguous slot: cut only at multiples of max_chunk; record the
+        // tensor holding each chunk's first element.
+        int t = 0;
+        int64_t a = 0;
+        for (int64_t soff = 0; soff < hi - lo; soff += max_chunk) {
+            const int64_t x = lo + soff;
+            while (a + numels[t] <= x) {
+                a += numels[t];
+                ++t;
+            }
+            const int64_t len = (hi - x) < max_chunk ? (hi - x) : max_chunk;
+            emit(soff, len, t, x - a, slot_dst + soff);
+        }
+    }
+    if (n_out)
+        *n_out = count;
+    if (shard_len_out)
+        *shard_len_out = S;
+    if (out && count > cap)
+        return ZERO_ERR_CAPACITY;
+    return ZERO_OK;
+}
+
+int zero_shard_step(const void *const *partials, int n_ranks, zero_dtype gdt,
+                    float *master, float *m, float *v, int64_t shard_len,
+                    const zero_chunk *d_chunks, int64_t n_chunks,
+                    const zero_adamw_hparams *hp, hipStream_t stream)
+{
+    StepArgs a;
+    int rc = check_partials(partials, n_ranks, gdt, shard_len, a.parts);
+    if (rc)
+        return rc;
+    if (((!master || !m || !v) && shard_len > 0) || shard_len < 0 || n_chunks < 0 ||
+        n_chunks > INT32_MAX ||
+        (n_chunks > 0 && !d_chunks) || !valid_hparams(hp))
+        return ZERO_ERR_INVALID;
+    if (!aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(d_chunks))
+        return ZERO_ERR_MISALIGNED;
+    const int64_t sb = shard_len * 4, gb = shard_len * elem_bytes(gdt);
+    if (overlaps(master, sb, m, sb) || overlaps(master, sb, v, sb) || overlaps(m, sb, v, sb))
+        return ZERO_ERR_ALIAS;
+    for (int k = 0; k < n_ranks; ++k)
+        if (overlaps(partials[k], gb, master, sb) || overlaps(partials[k], gb, m, sb) ||
+            overlaps(partials[k], gb, v, sb))
+            return ZERO_ERR_ALIAS;
+    if (n_chunks == 0 || shard_len == 0)
+        return ZERO_OK;
+    for (int k = 0; k < n_ranks; ++k)
+        if (!in_device_alloc(partials[k], gb))
+            return ZERO_ERR_NOT_DEVICE;
+    if (!in_device_alloc(master, sb) || !in_device_alloc(m, sb) || !in_device_alloc(v, sb) ||
+        !in_device_alloc(d_chunks, n_chunks * (int64_t)sizeof(zero_chunk)))
+        return ZERO_ERR_NOT_DEVICE;
+    a.red = make_reduce(n_ranks);
+    a.k = make_scalars(hp);
+    a.master = master;
+    a.m = m;
+    a.v = v;
+    a.chunks = d_chunks;
+    a.shard_len = shard_len;
+    return hip_status(launch_step(a, gdt, n_chunks, stream));
+}
+
+int zero_reduce_shard(const void *const *partials, int n_ranks, zero_dtype gdt, int64_t n,
+                      float *grad_out, hipStream_t stream)
+{
+    ReduceArgs a;
+    int rc = check_partials(partials, n_ranks, gdt, n, a.parts);
+    if (rc)
+        return rc;
+    if ((!grad_out && n > 0) || n < 0)
+        return ZERO_ERR_INVALID;
+    if (!aligned16(grad_out))
+        return ZERO_ERR_MISALIGNED;
+    for (int k = 0; k < n_ranks; ++k)
+        if (overlaps(partials[k], n * elem_bytes(gdt), grad_out, n * 4))
+            return ZERO_ERR_ALIAS;
+    if (n == 0)
+        return ZERO_OK;
+    for (int k = 0; k < n_ranks; ++k)
+        if (!in_device_alloc(partials[k], n * elem_bytes(gdt)))
+            return ZERO_ERR_NOT_DEVICE;
+    if (!in_device_alloc(grad_out, n * 4))
+        return ZERO_ERR_NOT_DEVICE;
+    a.red = make_reduce(n_ranks);
+    a.out = grad_out;
+    a.n = n;
+    return hip_status(launch_reduce(a, gdt, stream));
+}
+
+int zero_adamw_shard(const float *grad, float *master, float *m, float *v, int64_t n,
+                     const zero_adamw_hparams *hp, hipStream_t stream)
+{
+    if (((!grad || !master || !m || !v) && n > 0) || n < 0 || !valid_hparams(hp))
+        return ZERO_ERR_INVALID;
+    if (!aligned16(grad) || !aligned16(master) || !aligned16(m) || !aligned16(v))
+        return ZERO_ERR_MISALIGNED;
+    const int64_t b = n * 4;
+    if (overlaps(grad, b, master, b) || overlaps(grad, b, m, b) || overlaps(grad, b, v, b) ||
+        overlaps(master, b, m, b) || overlaps(master, b, v, b) || overlaps(m, b, v, b))
+        return ZERO_ERR_ALIAS;
+    if (n == 0)
+        return ZERO_OK;
+    if (!in_device_alloc(grad, b) || !in_device_alloc(master, b) || !in_device_alloc(m, b) ||
+        !in_device_alloc(v, b))
+        return ZERO_ERR_NOT_DEVICE;
+    AdamArgs a;
+    a.k = make_scalars(hp);
+    a.g = grad;
+    a.master = master;
+    a.m = m;
+    a.v = v;
+    a.n = n;
+    return hip_status(launch_adamw(a, stream));
+}
+
+int zero_gather_write(const float *master, int64_t shard_len, const zero_chunk *d_chunks,
+                      int64_t n_chunks, hipStream_t stream)
+{
+    if ((!master && shard_len > 0) || shard_len < 0 || n_chunks < 0 || n_chunks > INT32_MAX ||
+        (n_chunks > 0 && !d_chunks))
+        return ZERO_ERR_INVALID;
+    if (!aligned16(master) || !aligned16(d_chunks))
+        return ZERO_ERR_MISALIGNED;
+    if (n_chunks == 0 || shard_len == 0)
+        return ZERO_OK;
+    if (!in_device_alloc(master, shard_len * 4) ||
+        !in_device_alloc(d_chunks, n_chunks * (int64_t)sizeof(zero_chunk)))
+        return ZERO_ERR_NOT_DEVICE;
+    GatherArgs a;
+    a.master = master;
+    a.chunks = d_chunks;
+    a.shard_len = shard_len;
+    return hip_status(launch_gather(a, n_chunks, stream));
+}
+
+int zero_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream)
+{
+    if (((!src || !dst) && bytes > 0) || bytes < 0)
+        return ZERO_ERR_INVALID;
+    if (!aligned16(src) || !aligned16(dst))
+        return ZERO_ERR_MISALIGNED;
+    if (overlaps(src, bytes, dst, bytes))
+        return ZERO_ERR_ALIAS;
+    if (bytes == 0)
+        return ZERO_OK;
+    if (!in_device_alloc(src, bytes) || !in_device_alloc(dst, bytes))
+        return ZERO_ERR_NOT_DEVICE;
+    return hip_status(launch_probe_copy(src, dst, bytes, stream));
+}
+
+}  // extern "C"

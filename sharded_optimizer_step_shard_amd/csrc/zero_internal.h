@@ -1,0 +1,70 @@
+// Internal interface between the host API (zero_api.cpp) and the kernels
+// (zero_kernels.hip).  Not installed; the public ABI is include/zero_shard.h.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#include "zero_shard.h"
+
+namespace zs {
+
+// Step constants, each formed once on the host in double (see
+// make_scalars in zero_api.cpp); the kernels only combine them.
+struct StepScalars {
+    double b1, c1;     // beta1, 1 - beta1
+    double b2, c2;     // beta2, 1 - beta2
+    double bc1, bc2;   // 1 - beta1^t, 1 - beta2^t
+    double eps, lr;
+    double dec;        // 1 - lr * weight_decay
+};
+
+// Reduction constants: divide by N, or multiply by 1/N when N is a power
+// of two (exact scaling, so the same bits as the division).
+struct ReduceScalars {
+    double n;
+    double inv_n;
+    int pow2;
+    int n_ranks;
+};
+
+struct PartialPtrs {
+    const void *p[ZERO_MAX_RANKS];
+};
+
+struct StepArgs {
+    PartialPtrs parts;
+    ReduceScalars red;
+    StepScalars k;
+    float *master, *m, *v;
+    const zero_chunk *chunks;
+    int64_t shard_len;
+};
+
+struct ReduceArgs {
+    PartialPtrs parts;
+    ReduceScalars red;
+    float *out;
+    int64_t n;
+};
+
+struct AdamArgs {
+    StepScalars k;
+    const float *g;
+    float *master, *m, *v;
+    int64_t n;
+};
+
+struct GatherArgs {
+    const float *master;
+    const zero_chunk *chunks;
+    int64_t shard_len;
+};
+
+hipError_t launch_step(const StepArgs &a, zero_dtype gdt, int64_t n_chunks, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs &a, zero_dtype gdt, hipStream_t s);
+hipError_t launch_adamw(const AdamArgs &a, hipStream_t s);
+hipError_t launch_gather(const GatherArgs &a, int64_t n_chunks, hipStream_t s);
+hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s);
+
+}  // namespace zs

@@ -1,0 +1,445 @@
+// HIP kernels of the ZeRO shard step for gfx950 (CDNA4, wave64).
+//
+// The step is a pure stream: every shard element is read once from each of
+// the N gradient partials and from the fp32 master, m and v, and written
+// once to master, m, v and the bf16 parameter slot.  Nothing is reused, so
+// the bound is HBM bandwidth: (2N + 26) bytes per element with bf16
+// partials, (4N + 26) with fp32 partials.  There is no contraction here,
+// so no MFMA; the kernels are built around 16-byte per-lane accesses that
+// a wave turns into fully coalesced 1 KiB requests.
+//
+// Work split: one workgroup (256 lanes, 4 waves) per chunk of the chunk
+// table.  A lane handles a group of VEC consecutive elements (8 with bf16
+// partials: one 16-byte load per partial; 4 with fp32 partials), strided by
+// the workgroup size.  Groups sit on the shard's VEC-element grid, so all
+// partial and state loads are 16-byte aligned; a chunk that starts or ends
+// off the grid handles its first or last group element by element.
+//
+// Arithmetic follows the fixed evaluation order in include/zero_shard.h:
+// double sums in rank order, IEEE double AdamW without contraction (the
+// library is built with -ffp-contract=off), one rounding per stored value.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero_internal.h"
+
+namespace zs {
+
+constexpr int kBlock = 256;
+
+// Native clang vectors: 16-byte (and 8-byte) loads and stores, and the
+// non-temporal store builtin, need them rather than HIP's struct wrappers.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ double bf16_lo(uint32_t w) { return (double)__uint_as_float(w << 16); }
+__device__ __forceinline__ double bf16_hi(uint32_t w) { return (double)__uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even.  Adding 0x7FFF plus the lowest kept
+// bit carries into the kept half exactly when the dropped half is above
+// one half, or equal to it with an odd kept half.  NaN: keep sign and top
+// payload, set the quiet bit.
+__device__ __forceinline__ uint32_t to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : r;
+}
+
+// Sum -> fp32 mean.  With N a compile-time power of two the division is a
+// multiplication by the exact 1/N (same bits); otherwise the host's pow2
+// flag picks it at run time.
+template <int NC>
+__device__ __forceinline__ float finish_reduce(double s, const ReduceScalars &r)
+{
+    if constexpr (NC > 0 && (NC & (NC - 1)) == 0)
+        return (float)(s * r.inv_n);
+    else
+        return (float)(r.pow2 ? s * r.inv_n : s / r.n);
+}
+
+__device__ __forceinline__ void adamw(float g32, float &th, float &m, float &v, const StepScalars &k)
+{
+    double g = (double)g32;
+    double m1 = k.b1 * (double)m + k.c1 * g;
+    double v1 = k.b2 * (double)v + k.c2 * (g * g);
+    double mhat = m1 / k.bc1;
+    double vhat = v1 / k.bc2;
+    double upd = mhat / (__builtin_sqrt(vhat) + k.eps);
+    double t1 = (double)th * k.dec - k.lr * upd;
+    m = (float)m1;
+    v = (float)v1;
+    th = (float)t1;
+}
+
+template <typename T>
+__device__ __forceinline__ T ld(const T *p) { return *p; }
+
+template <typename T>
+__device__ __forceinline__ void st_nt(T *p, T x) { __builtin_nontemporal_store(x, p); }
+
+// Per gradient dtype: group width and how a 16-byte raw vector widens.
+template <zero_dtype G> struct Grad;
+
+template <> struct Grad<ZERO_BF16> {
+    static constexpr int VEC = 8;
+    static constexpr int BYTES = 2;
+    __device__ static __forceinline__ void first(double *s, u32x4 r)
+    {
+        s[0] = bf16_lo(r.x); s[1] = bf16_hi(r.x); s[2] = bf16_lo(r.y); s[3] = bf16_hi(r.y);
+        s[4] = bf16_lo(r.z); s[5] = bf16_hi(r.z); s[6] = bf16_lo(r.w); s[7] = bf16_hi(r.w);
+    }
+    __device__ static __forceinline__ void add(double *s, u32x4 r)
+    {
+        s[0] = s[0] + bf16_lo(r.x); s[1] = s[1] + bf16_hi(r.x);
+        s[2] = s[2] + bf16_lo(r.y); s[3] = s[3] + bf16_hi(r.y);
+        s[4] = s[4] + bf16_lo(r.z); s[5] = s[5] + bf16_hi(r.z);
+        s[6] = s[6] + bf16_lo(r.w); s[7] = s[7] + bf16_hi(r.w);
+    }
+    __device__ static __forceinline__ double one(const void *p, int64_t i)
+    {
+        return (double)__uint_as_float((uint32_t)((const uint16_t *)p)[i] << 16);
+    }
+};
+
+template <> struct Grad<ZERO_FP32> {
+    static constexpr int VEC = 4;
+    static constexpr int BYTES = 4;
+    __device__ static __forceinline__ void first(double *s, u32x4 r)
+    {
+        s[0] = (double)__uint_as_float(r.x); s[1] = (double)__uint_as_float(r.y);
+        s[2] = (double)__uint_as_float(r.z); s[3] = (double)__uint_as_float(r.w);
+    }
+    __device__ static __forceinline__ void add(double *s, u32x4 r)
+    {
+        s[0] = s[0] + (double)__uint_as_float(r.x); s[1] = s[1] + (double)__uint_as_float(r.y);
+        s[2] = s[2] + (double)__uint_as_float(r.z); s[3] = s[3] + (double)__uint_as_float(r.w);
+    }
+    __device__ static __forceinline__ double one(const void *p, int64_t i)
+    {
+        return (double)((const float *)p)[i];
+    }
+};
+
+__device__ __forceinline__ u32x4 ld_raw(const void *base, int64_t byte_off)
+{
+    return ld((const u32x4 *)((const char *)base + byte_off));
+}
+
+// Sum of the N partials over one full group starting at element i0, in
+// rank order.  NC > 0: N known at compile time (loads issued in batches of
+// up to 16 before their adds); NC == 0: N at run time.
+template <zero_dtype G, int NC>
+__device__ __forceinline__ void group_sum(double *s, const PartialPtrs &pp, int n_rt, int64_t i0)
+{
+    using GT = Grad<G>;
+    const int64_t off = i0 * GT::BYTES;
+    if constexpr (NC > 0) {
+        constexpr int B = NC < 16 ? NC : 16;
+#pragma unroll
+        for (int kb = 0; kb < NC; kb += B) {
+            u32x4 raw[B];
+#pragma unroll
+            for (int j = 0; j < B; ++j)
+                raw[j] = ld_raw(pp.p[kb + j], off);
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                if (kb + j == 0)
+                    GT::first(s, raw[j]);
+                else
+                    GT::add(s, raw[j]);
+            }
+        }
+    } else {
+        GT::first(s, ld_raw(pp.p[0], off));
+#pragma unroll 4
+        for (int k = 1; k < n_rt; ++k)
+            GT::add(s, ld_raw(pp.p[k], off));
+    }
+}
+
+template <zero_dtype G>
+__device__ __forceinline__ double elem_sum(const PartialPtrs &pp, int n, int64_t i)
+{
+    double s = Grad<G>::one(pp.p[0], i);
+    for (int k = 1; k < n; ++k)
+        s = s + Grad<G>::one(pp.p[k], i);
+    return s;
+}
+
+// VEC fp32 values (4 or 8) at a 16-byte aligned address, moved with
+// 16-byte loads and non-temporal 16-byte stores.
+template <int VEC> struct F32x {
+    float e[VEC];
+    __device__ __forceinline__ void load(const float *p)
+    {
+#pragma unroll
+        for (int q = 0; q < VEC / 4; ++q) {
+            f32x4 t = ld((const f32x4 *)p + q);
+            e[4 * q + 0] = t.x; e[4 * q + 1] = t.y; e[4 * q + 2] = t.z; e[4 * q + 3] = t.w;
+        }
+    }
+    __device__ __forceinline__ void store(float *p) const
+    {
+#pragma unroll
+        for (int q = 0; q < VEC / 4; ++q) {
+            f32x4 t = {e[4 * q + 0], e[4 * q + 1], e[4 * q + 2], e[4 * q + 3]};
+            st_nt((f32x4 *)p + q, t);
+        }
+    }
+    __device__ __forceinline__ float &operator[](int j) { return e[j]; }
+};
+
+// VEC bf16 values: one 16-byte (VEC = 8) or 8-byte (VEC = 4) store when the
+// destination is aligned for it, else element by element.
+template <int VEC>
+__device__ __forceinline__ void store_bf16(uint16_t *dst, const uint32_t *h, bool vec_ok)
+{
+    if (vec_ok) {
+        if constexpr (VEC == 8) {
+            u32x4 w = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+            st_nt((u32x4 *)dst, w);
+        } else {
+            u32x2 w = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+            st_nt((u32x2 *)dst, w);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            dst[j] = (uint16_t)h[j];
+    }
+}
+
+// ---------------------------------------------------------------- fused step
+
+template <zero_dtype G, int NC>
+__global__ __launch_bounds__(kBlock) void shard_step_kernel(StepArgs a)
+{
+    constexpr int VEC = Grad<G>::VEC;
+    const zero_chunk c = a.chunks[blockIdx.x];
+    if (c.len <= 0 || c.shard_off < 0 || c.shard_off > a.shard_len - c.len)
+        return;
+    const int n = NC > 0 ? NC : a.red.n_ranks;
+    const int64_t lo = c.shard_off, hi = c.shard_off + c.len;
+    const int64_t g0 = lo / VEC, g1 = (hi + VEC - 1) / VEC;
+    // dst address of the first element of group g0, aligned for a vector store?
+    const bool vec_ok = (((uintptr_t)c.dst - (uintptr_t)(2 * (lo - g0 * VEC))) % (2 * VEC)) == 0;
+
+    for (int64_t g = g0 + threadIdx.x; g < g1; g += kBlock) {
+        const int64_t i0 = g * VEC;
+        uint16_t *d = c.dst + (i0 - lo);
+        if (i0 >= lo && i0 + VEC <= hi) {
+            double s[VEC];
+            group_sum<G, NC>(s, a.parts, n, i0);
+            F32x<VEC> th, m, v;
+            th.load(a.master + i0);
+            m.load(a.m + i0);
+            v.load(a.v + i0);
+            uint32_t h[VEC];
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                float gj = finish_reduce<NC>(s[j], a.red);
+                adamw(gj, th[j], m[j], v[j], a.k);
+                h[j] = to_bf16(th[j]);
+            }
+            th.store(a.master + i0);
+            m.store(a.m + i0);
+            v.store(a.v + i0);
+            store_bf16<VEC>(d, h, vec_ok);
+        } else {
+            for (int j = 0; j < VEC; ++j) {
+                const int64_t i = i0 + j;
+                if (i < lo || i >= hi)
+                    continue;
+                float gj = finish_reduce<NC>(elem_sum<G>(a.parts, n, i), a.red);
+                float th = a.master[i], m = a.m[i], v = a.v[i];
+                adamw(gj, th, m, v, a.k);
+                a.master[i] = th;
+                a.m[i] = m;
+                a.v[i] = v;
+                d[j] = (uint16_t)to_bf16(th);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- unfused
+
+template <zero_dtype G, int NC>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a)
+{
+    constexpr int VEC = Grad<G>::VEC;
+    const int n = NC > 0 ? NC : a.red.n_ranks;
+    const int64_t groups = a.n / VEC;
+    for (int64_t g = (int64_t)blockIdx.x * kBlock + threadIdx.x; g < groups;
+         g += (int64_t)gridDim.x * kBlock) {
+        const int64_t i0 = g * VEC;
+        double s[VEC];
+        group_sum<G, NC>(s, a.parts, n, i0);
+        F32x<VEC> out;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            out[j] = finish_reduce<NC>(s[j], a.red);
+        out.store(a.out + i0);
+    }
+    if (blockIdx.x == 0) {
+        const int64_t i = groups * VEC + threadIdx.x;
+        if (i < a.n)
+            a.out[i] = finish_reduce<NC>(elem_sum<G>(a.parts, n, i), a.red);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void adamw_kernel(AdamArgs a)
+{
+    const int64_t groups = a.n / 4;
+    for (int64_t g = (int64_t)blockIdx.x * kBlock + threadIdx.x; g < groups;
+         g += (int64_t)gridDim.x * kBlock) {
+        const int64_t i0 = g * 4;
+        F32x<4> gr, th, m, v;
+        gr.load(a.g + i0);
+        th.load(a.master + i0);
+        m.load(a.m + i0);
+        v.load(a.v + i0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            adamw(gr[j], th[j], m[j], v[j], a.k);
+        th.store(a.master + i0);
+        m.store(a.m + i0);
+        v.store(a.v + i0);
+    }
+    if (blockIdx.x == 0) {
+        const int64_t i = groups * 4 + threadIdx.x;
+        if (i < a.n) {
+            float th = a.master[i], m = a.m[i], v = a.v[i];
+            adamw(a.g[i], th, m, v, a.k);
+            a.master[i] = th;
+            a.m[i] = m;
+            a.v[i] = v;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
+{
+    constexpr int VEC = 8;
+    const zero_chunk c = a.chunks[blockIdx.x];
+    if (c.len <= 0 || c.shard_off < 0 || c.shard_off > a.shard_len - c.len)
+        return;
+    const int64_t lo = c.shard_off, hi = c.shard_off + c.len;
+    const int64_t g0 = lo / VEC, g1 = (hi + VEC - 1) / VEC;
+    const bool vec_ok = (((uintptr_t)c.dst - (uintptr_t)(2 * (lo - g0 * VEC))) % (2 * VEC)) == 0;
+    for (int64_t g = g0 + threadIdx.x; g < g1; g += kBlock) {
+        const int64_t i0 = g * VEC;
+        uint16_t *d = c.dst + (i0 - lo);
+        if (i0 >= lo && i0 + VEC <= hi) {
+            F32x<VEC> th;
+            th.load(a.master + i0);
+            uint32_t h[VEC];
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+                h[j] = to_bf16(th[j]);
+            store_bf16<VEC>(d, h, vec_ok);
+        } else {
+            for (int j = 0; j < VEC; ++j) {
+                const int64_t i = i0 + j;
+                if (i >= lo && i < hi)
+                    d[j] = (uint16_t)to_bf16(a.master[i]);
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void probe_copy_kernel(const u32x4 *src, u32x4 *dst, int64_t n16,
+                                                            const uint8_t *src_b, uint8_t *dst_b,
+                                                            int64_t bytes)
+{
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n16; i += (int64_t)gridDim.x * kBlock)
+        st_nt(dst + i, ld(src + i));
+    if (blockIdx.x == 0) {
+        const int64_t b = n16 * 16 + threadIdx.x;
+        if (b < bytes)
+            dst_b[b] = src_b[b];
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+
+static int grid_for(int64_t items)
+{
+    // Enough workgroups to fill 256 CUs many times over; the kernels stride.
+    int64_t blocks = (items + kBlock - 1) / kBlock;
+    if (blocks > 256 * 64)
+        blocks = 256 * 64;
+    return blocks < 1 ? 1 : (int)blocks;
+}
+
+template <zero_dtype G>
+static hipError_t step_dispatch(const StepArgs &a, int64_t n_chunks, hipStream_t s)
+{
+    dim3 grid((unsigned)n_chunks), block(kBlock);
+    switch (a.red.n_ranks) {
+    case 1: hipLaunchKernelGGL((shard_step_kernel<G, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((shard_step_kernel<G, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((shard_step_kernel<G, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((shard_step_kernel<G, 8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((shard_step_kernel<G, 16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((shard_step_kernel<G, 32>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((shard_step_kernel<G, 64>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((shard_step_kernel<G, 0>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_step(const StepArgs &a, zero_dtype gdt, int64_t n_chunks, hipStream_t s)
+{
+    return gdt == ZERO_BF16 ? step_dispatch<ZERO_BF16>(a, n_chunks, s)
+                            : step_dispatch<ZERO_FP32>(a, n_chunks, s);
+}
+
+template <zero_dtype G>
+static hipError_t reduce_dispatch(const ReduceArgs &a, hipStream_t s)
+{
+    dim3 grid(grid_for(a.n / Grad<G>::VEC + 1)), block(kBlock);
+    switch (a.red.n_ranks) {
+    case 1: hipLaunchKernelGGL((reduce_kernel<G, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((reduce_kernel<G, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((reduce_kernel<G, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((reduce_kernel<G, 8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((reduce_kernel<G, 16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((reduce_kernel<G, 32>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((reduce_kernel<G, 64>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((reduce_kernel<G, 0>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReduceArgs &a, zero_dtype gdt, hipStream_t s)
+{
+    return gdt == ZERO_BF16 ? reduce_dispatch<ZERO_BF16>(a, s) : reduce_dispatch<ZERO_FP32>(a, s);
+}
+
+hipError_t launch_adamw(const AdamArgs &a, hipStream_t s)
+{
+    hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(a.n / 4 + 1)), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs &a, int64_t n_chunks, hipStream_t s)
+{
+    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)n_chunks), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s)
+{
+    const int64_t n16 = bytes / 16;
+    hipLaunchKernelGGL(probe_copy_kernel, dim3(grid_for(n16 + 1)), dim3(kBlock), 0, s,
+                       (const u32x4 *)src, (u32x4 *)dst, n16, (const uint8_t *)src, (uint8_t *)dst, bytes);
+    return hipGetLastError();
+}
+
+}  // namespace zs

@@ -50,7 +50,67 @@ def build(verbose: bool = False) -> None:
     subprocess.run(cmd, check=True)
 
 
+def build_dev(verbose: bool = False) -> None:
+    """Compile the device twin (fill.hip) for gfx950 with hipcc."""
+    cmd = ["/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc",
+           "--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-ffp-contract=off",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument", "-o", DEV_LIB, os.path.join(_HERE, "fill.hip")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
 _host = None
+_dev = None
+
+
+def _devlib():
+    global _dev
+    if _dev is None:
+        if not os.path.exists(DEV_LIB):
+            raise ImportError(f"{DEV_LIB} missing: run synth.build_dev() (hipcc)")
+        lib = ctypes.CDLL(DEV_LIB)
+        u64, i64, f32, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+        for name in ("synth_dev_fill_f32", "synth_dev_fill_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp, u64, u64, i64, i64, f32, u64, f32, f32, vp]
+            fn.restype = ctypes.c_int
+        lib.synth_dev_spread.argtypes = [vp, vp, i64, u64, u64, i64, i64, vp]
+        lib.synth_dev_spread.restype = ctypes.c_int
+        _dev = lib
+    return _dev
+
+
+def dev_fill(out, seed: int, stream: int, start: int, sigma: float, mask_stream: int = 0,
+             frac: float = 0.0, mult: float = 1.0) -> None:
+    """Fill a contiguous device tensor (bf16/int16 -> bf16 bits, float32) with
+    the values at global indices [start, start + out.numel()), on the current
+    torch stream."""
+    import torch
+    assert out.is_cuda and out.is_contiguous()
+    st = torch.cuda.current_stream().cuda_stream
+    if out.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        fn = _devlib().synth_dev_fill_bf16
+    elif out.dtype == torch.float32:
+        fn = _devlib().synth_dev_fill_f32
+    else:
+        raise TypeError(out.dtype)
+    rc = fn(out.data_ptr(), seed, stream, start, out.numel(), scale_for_std(sigma), mask_stream,
+            frac, mult, st)
+    if rc:
+        raise RuntimeError("synth device fill failed to launch")
+
+
+def dev_spread(dst, prefix, seed: int, stream: int, start: int) -> None:
+    """dst[j] = prefix[src(start + j)] on the device (warm-start spreading)."""
+    import torch
+    assert dst.is_cuda and prefix.is_cuda and dst.dtype == prefix.dtype == torch.float32
+    rc = _devlib().synth_dev_spread(dst.data_ptr(), prefix.data_ptr(), prefix.numel(), seed,
+                                    stream, start, dst.numel(),
+                                    torch.cuda.current_stream().cuda_stream)
+    if rc:
+        raise RuntimeError("synth device spread failed to launch")
 
 
 def _lib():

@@ -157,3 +157,25 @@ ALL = {"tiny": tiny, "gpt2": gpt2, "llama7b": llama7b, "llama70b": llama70b, "ra
 
 def get(name: str) -> Workload:
     return ALL[name]()
+
+
+def zero_ranges(w: Workload, lo: int, hi: int) -> List[Tuple[int, int]]:
+    """Shard-relative [a, b) ranges of [lo, hi) whose gradients are all zero."""
+    out = []
+    start = 0
+    zs = set(w.zero_tensors)
+    for t, n in enumerate(w.numels):
+        a, b = start, start + n
+        start = b
+        if t in zs and b > lo and a < hi:
+            out.append((max(a, lo) - lo, min(b, hi) - lo))
+    return out
+
+
+def zero_mask(w: Workload, flat_idx: np.ndarray) -> np.ndarray:
+    """True where a global flat index lies in a tensor with all-zero gradients."""
+    if not w.zero_tensors:
+        return np.zeros(np.shape(flat_idx), dtype=bool)
+    starts = np.cumsum([0] + w.numels[:-1])
+    t = np.searchsorted(starts, flat_idx, side="right") - 1
+    return np.isin(t, np.asarray(w.zero_tensors))

@@ -1,0 +1,221 @@
+"""The C-ABI boundary, on the CPU: the library loads and exports every entry
+point the header declares; host-side checks return the documented codes
+before anything is launched; the chunk table matches the oracle's shard
+geometry.  No call here reaches a kernel launch (every call either fails a
+host check or has nothing to do), so no GPU is needed and any addresses
+passed are never dereferenced."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zero_shard.h")
+
+
+@pytest.fixture(scope="module")
+def zs():
+    import sharded_optimizer_step_shard_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(zero_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    fns = declared_functions()
+    for name in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
+                 "zero_gather_write", "zero_strerror", "zero_version", "zero_probe_copy"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(zs):
+    out = subprocess.run(["nm", "-D", "--defined-only", zs.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(zs.lib(), name)
+
+
+def test_version_and_strerror(zs):
+    assert zs.zero_version() == (1, 0)
+    for code in range(8):
+        assert zs.zero_strerror(code) and zs.zero_strerror(code) != "unknown error code"
+    assert zs.zero_strerror(99) == "unknown error code"
+
+
+def test_struct_layouts(zs):
+    assert zs.CHUNK_DTYPE.itemsize == 32
+    assert [zs.CHUNK_DTYPE.fields[f][1] for f in ("shard_off", "dst", "len", "tensor_id", "tensor_off")] \
+        == [0, 8, 16, 20, 24]
+    assert ctypes.sizeof(zs.HParams) == 48
+
+
+# A fake, aligned, never-dereferenced device address space for argument checks.
+BASE = 0x7F0000000000
+
+
+def parts(n_ranks, stride=1 << 30, base=BASE):
+    return (ctypes.c_void_p * max(n_ranks, 1))(*[base + k * stride for k in range(n_ranks)])
+
+
+def step(zs, p, n_ranks, gdt=0, master=BASE + (1 << 40), m=BASE + (1 << 40) + (1 << 32),
+         v=BASE + (1 << 40) + (2 << 32), n=1000, chunks=BASE + (1 << 41), n_chunks=1, hp=None):
+    hp = zs.hparams(1) if hp is None else hp
+    return zs.raw_call("zero_shard_step", p, n_ranks, gdt, master, m, v, n, chunks, n_chunks,
+                       ctypes.byref(hp), None)
+
+
+def test_shard_step_argument_errors(zs):
+    E = zs
+    assert step(zs, None, 4) == E.ZERO_ERR_INVALID
+    assert step(zs, parts(4), 0) == E.ZERO_ERR_INVALID
+    assert step(zs, parts(65), 65) == E.ZERO_ERR_INVALID
+    assert step(zs, parts(4), 4, gdt=7) == E.ZERO_ERR_UNSUPPORTED
+    bad = parts(4)
+    bad[2] = None
+    assert step(zs, bad, 4) == E.ZERO_ERR_INVALID
+    bad[2] = BASE + 2 * (1 << 30) + 2
+    assert step(zs, bad, 4) == E.ZERO_ERR_MISALIGNED
+    assert step(zs, parts(4), 4, master=None) == E.ZERO_ERR_INVALID
+    assert step(zs, parts(4), 4, v=BASE + (1 << 40) + (2 << 32) + 4) == E.ZERO_ERR_MISALIGNED
+    assert step(zs, parts(4), 4, chunks=BASE + (1 << 41) + 8) == E.ZERO_ERR_MISALIGNED
+    assert step(zs, parts(4), 4, n=-1) == E.ZERO_ERR_INVALID
+    assert step(zs, parts(4), 4, n_chunks=-1) == E.ZERO_ERR_INVALID
+    assert step(zs, parts(4), 4, chunks=None) == E.ZERO_ERR_INVALID
+    for hp in (zs.hparams(0), zs.hparams(1, beta1=1.0), zs.hparams(1, beta2=-0.1),
+               zs.hparams(1, lr=float("nan")), zs.hparams(1, eps=float("inf"))):
+        assert step(zs, parts(4), 4, hp=hp) == E.ZERO_ERR_INVALID
+    # aliasing: a partial over master, m over v, partial overlapping m by one element
+    assert step(zs, parts(4), 4, master=BASE) == E.ZERO_ERR_ALIAS
+    assert step(zs, parts(4), 4, v=BASE + (1 << 40) + (1 << 32) + 16) == E.ZERO_ERR_ALIAS
+    assert step(zs, parts(4, base=BASE + (1 << 40) + (1 << 32) - 2 * 1000 + 16), 4,
+                n=1000) == E.ZERO_ERR_ALIAS
+    assert step(zs, parts(4), 4, gdt=1, master=BASE + 3008, n=1000,
+                ) == E.ZERO_ERR_ALIAS   # fp32 partial 0 is 4000 bytes long
+
+
+def test_non_device_addresses_are_rejected(zs):
+    """Calls that pass every other check but name memory that is not a device
+    allocation (here: fake addresses, or host memory) return NOT_DEVICE and
+    launch nothing."""
+    hp = zs.hparams(1)
+    assert step(zs, parts(4), 4) == zs.ZERO_ERR_NOT_DEVICE
+    a = BASE + (1 << 40)
+    assert zs.raw_call("zero_adamw_shard", a, a + 8192, a + 16384, a + 24576, 1024,
+                       ctypes.byref(hp), None) == zs.ZERO_ERR_NOT_DEVICE
+    assert zs.raw_call("zero_reduce_shard", parts(2), 2, 0, 10, a, None) == zs.ZERO_ERR_NOT_DEVICE
+    assert zs.raw_call("zero_gather_write", a, 10, a + 4096, 1, None) == zs.ZERO_ERR_NOT_DEVICE
+    host = np.zeros(1024, np.float32)
+    assert zs.raw_call("zero_probe_copy", host.ctypes.data, a, 1024, None) == zs.ZERO_ERR_NOT_DEVICE
+
+
+def test_empty_calls_are_noops(zs):
+    assert step(zs, parts(4), 4, n=0) == zs.ZERO_OK
+    assert step(zs, parts(4), 4, n_chunks=0, chunks=None) == zs.ZERO_OK
+    nulls = (ctypes.c_void_p * 4)(None, None, None, None)
+    assert step(zs, nulls, 4, master=None, m=None, v=None, n=0, chunks=None, n_chunks=0) == zs.ZERO_OK
+    assert zs.raw_call("zero_reduce_shard", nulls, 4, 0, 0, None, None) == zs.ZERO_OK
+    hp = zs.hparams(1)
+    assert zs.raw_call("zero_adamw_shard", None, None, None, None, 0, ctypes.byref(hp), None) == 0
+    assert zs.raw_call("zero_gather_write", None, 0, None, 0, None) == zs.ZERO_OK
+    assert zs.raw_call("zero_probe_copy", None, None, 0, None) == zs.ZERO_OK
+
+
+def test_unfused_argument_errors(zs):
+    hp = zs.hparams(1)
+    p = parts(2)
+    assert zs.raw_call("zero_reduce_shard", p, 2, 0, 10, None, None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_reduce_shard", p, 2, 0, 10, BASE + 4, None) == zs.ZERO_ERR_MISALIGNED
+    assert zs.raw_call("zero_reduce_shard", p, 2, 0, 10, BASE + 16, None) == zs.ZERO_ERR_ALIAS
+    assert zs.raw_call("zero_reduce_shard", p, 2, 9, 10, BASE + (1 << 40), None) == zs.ZERO_ERR_UNSUPPORTED
+    a = BASE + (1 << 40)
+    assert zs.raw_call("zero_adamw_shard", a, a + 2048, a + 8192, a + 12288, 1024,
+                       ctypes.byref(hp), None) == zs.ZERO_ERR_ALIAS
+    assert zs.raw_call("zero_adamw_shard", a, a + 8192, a + 16384, a + 24576, 1024,
+                       ctypes.byref(zs.hparams(0)), None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_gather_write", a + 8, 10, a + 4096, 1, None) == zs.ZERO_ERR_MISALIGNED
+    assert zs.raw_call("zero_gather_write", a, -1, a + 4096, 1, None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_probe_copy", a, a + 64, 128, None) == zs.ZERO_ERR_ALIAS
+
+
+# ---------------------------------------------------------------- chunk table
+
+def expand(table):
+    """Per shard element: (tensor id, offset in tensor, dst address)."""
+    rows = []
+    for c in table:
+        j = np.arange(c["len"], dtype=np.int64)
+        rows.append(np.stack([np.full(c["len"], c["tensor_id"]), c["tensor_off"] + j,
+                              c["shard_off"] + j, c["dst"].astype(np.int64) + 2 * j], 1))
+    return np.concatenate(rows) if rows else np.zeros((0, 4), np.int64)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_chunk_table_matches_oracle_geometry(zs, seed):
+    rng = np.random.default_rng(seed)
+    numels = [int(x) for x in rng.integers(1, 5000, rng.integers(1, 30))]
+    n_ranks = int(rng.integers(1, 12))
+    max_chunk = int(rng.choice([64, 128, 640, 65536]))
+    bases = [BASE + (t << 24) for t in range(len(numels))]
+    for rank in range(n_ranks):
+        seg, S = oracle.shard_segments(numels, n_ranks, rank)
+        want_t = np.concatenate([np.full(s[3], s[0]) for s in seg]) if len(seg) else np.zeros(0)
+        want_off = np.concatenate([s[1] + np.arange(s[3]) for s in seg]) if len(seg) else np.zeros(0)
+        # tensor destinations
+        table, S2 = zs.zero_build_chunks(numels, n_ranks, rank, tensor_dst=bases, max_chunk=max_chunk)
+        assert S2 == S
+        e = expand(table)
+        assert np.array_equal(e[:, 2], np.arange(len(want_t)))          # in order, exactly once
+        assert np.array_equal(e[:, 0], want_t) and np.array_equal(e[:, 1], want_off)
+        assert np.array_equal(e[:, 3], np.array(bases)[e[:, 0].astype(int)] + 2 * e[:, 1])
+        assert np.all(table["len"] <= max_chunk) and np.all(table["len"] >= 1)
+        assert np.all((table["shard_off"] // max_chunk) ==
+                      ((table["shard_off"] + table["len"] - 1) // max_chunk))
+        # slot destination
+        slot = BASE + (1 << 40)
+        table, _ = zs.zero_build_chunks(numels, n_ranks, rank, slot_dst=slot, max_chunk=max_chunk)
+        e = expand(table)
+        assert np.array_equal(e[:, 2], np.arange(len(want_t)))
+        assert np.array_equal(e[:, 3], slot + 2 * e[:, 2])
+        assert np.array_equal(table["tensor_id"], want_t[table["shard_off"]].astype(np.int32))
+        assert np.array_equal(table["tensor_off"], want_off[table["shard_off"]])
+
+
+def test_chunk_table_errors(zs):
+    nm = np.array([10, 20], dtype=np.int64)
+    n = ctypes.c_int64(0)
+    S = ctypes.c_int64(0)
+    call = lambda *a: zs.raw_call("zero_build_chunks", *a)  # noqa: E731
+    assert call(nm.ctypes.data, 2, 2, 2, None, BASE, 64, None, 0, None, None) == zs.ZERO_ERR_INVALID
+    assert call(nm.ctypes.data, 2, 2, 0, None, None, 64, None, 0, None, None) == zs.ZERO_ERR_INVALID
+    assert call(nm.ctypes.data, 2, 2, 0, None, BASE, 100, None, 0, None, None) == zs.ZERO_ERR_INVALID
+    assert call(nm.ctypes.data, 2, 0, 0, None, BASE, 64, None, 0, None, None) == zs.ZERO_ERR_INVALID
+    assert call(nm.ctypes.data, 2, 1, 0, None, BASE, 64, None, 0, ctypes.byref(n), ctypes.byref(S)) == 0
+    assert n.value == 1 and S.value == 30
+    out = np.zeros(4, dtype=zs.CHUNK_DTYPE)
+    big = np.array([1000], dtype=np.int64)
+    assert call(big.ctypes.data, 1, 1, 0, None, BASE, 64, out.ctypes.data, 4, ctypes.byref(n),
+                None) == zs.ZERO_ERR_CAPACITY
+    assert n.value == 16 and out["len"][3] == 64
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    """No silent fallback: the package refuses to import without its .so."""
+    import shutil
+    pkg = os.path.join(ROOT, "sharded_optimizer_step_shard_amd")
+    dst = tmp_path / "sharded_optimizer_step_shard_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    r = subprocess.run([sys.executable, "-c", "import sharded_optimizer_step_shard_amd"],
+                       cwd=tmp_path, capture_output=True, text=True)
+    assert r.returncode != 0 and "missing" in r.stderr

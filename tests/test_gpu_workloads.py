@@ -1,0 +1,137 @@
+"""GPU parity at the workloads' real sizes, in the configuration bench.py
+times (its Shard setup: device-filled inputs, chunk table, launch).
+
+GPT-2 and the ragged fp32 case are compared in full; the 7B and 70B
+shards on sampled indices that the oracle replays one by one (every chunk
+boundary +-8, the first and last 4096 elements, 65,536 hashed indices).
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import workloads as W
+from gpu_helpers import check_state, host_master, host_partials, oracle_warm_prefix, sample_indices, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bench():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bench as b
+    return b
+
+
+def host(t):
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+def release():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def gather_state(sh, idx):
+    i = torch.from_numpy(idx).to(sh.dev)
+    return (sh.master[i].cpu().numpy(), sh.m[i].cpu().numpy(), sh.v[i].cpu().numpy(),
+            sh.param_at(idx))
+
+
+def test_gpt2_full_twenty_steps(bench):
+    w = W.gpt2()
+    say(f"case: {w.name} rank 3, {w.steps} steps, full compare")
+    sh = bench.Shard(w, rank=3)
+    idx = np.arange(sh.lo, sh.hi, dtype=np.int64)
+    th = host_master(w, idx)
+    m = np.zeros(sh.n, np.float32)
+    v = np.zeros(sh.n, np.float32)
+    for t in range(1, w.steps + 1):
+        sh.fill_partials(t)
+        sh.step(t)
+        parts = host_partials(w, t, idx)
+        th, m, v, p = oracle.shard_step(parts, th, m, v, oracle.hparams(t, **w.hparams()))
+        if t in (1, 2, 10, w.steps):
+            say(f"  step {t}: compare")
+            flat = np.concatenate([host(x) for x in sh.params])
+            check_state((host(sh.master), host(sh.m), host(sh.v), flat[sh.lo:sh.hi]),
+                        (th, m, v, p), f"gpt2 step {t}")
+    del sh
+    release()
+
+
+def test_ragged_fp32_full(bench):
+    w = W.ragged()
+    say(f"case: {w.name} rank 0, 2 steps, full compare ({len(w.zero_tensors)} zero tensors)")
+    sh = bench.Shard(w, rank=0)
+    idx = np.arange(sh.lo, sh.hi, dtype=np.int64)
+    th = host_master(w, idx)
+    m = np.zeros(sh.n, np.float32)
+    v = np.zeros(sh.n, np.float32)
+    for t in (1, 2):
+        sh.fill_partials(t)
+        sh.step(t)
+        parts = host_partials(w, t, idx)
+        oracle.shard_step(parts, th, m, v, oracle.hparams(t, **w.hparams()), in_place=True)
+        del parts
+    p = oracle.bf16_round(th)
+    flat = np.concatenate([host(x) for x in sh.params])
+    check_state((host(sh.master), host(sh.m), host(sh.v), flat[sh.lo:sh.hi]), (th, m, v, p),
+                "ragged step 2")
+    del sh
+    release()
+
+
+def test_llama7b_warm_start_and_sampled_steps(bench):
+    w = W.llama7b()
+    say(f"case: {w.name} rank 0: warm start ({w.warm_steps} steps on {w.warm_prefix}), "
+        "then 3 bench steps, sampled compare")
+    sh = bench.Shard(w, rank=0)
+    t0 = sh.prepare()
+    assert t0 == w.warm_steps + 1
+    P = w.warm_prefix
+    pth, pm, pv = oracle_warm_prefix(w, sh.lo)
+    say("  warm-start prefix: full compare against the oracle's own prefix run")
+    check_state((host(sh.master[:P]), host(sh.m[:P]), host(sh.v[:P])), (pth, pm, pv),
+                "7b warm prefix")
+    steps = [t0, t0 + 1, t0 + 2]
+    for t in steps:
+        sh.step(t)
+    idx = sample_indices(sh.table, sh.n, seed=7)
+    say(f"  {idx.size} sampled indices")
+    src = synth.prefix_src(w.seed, synth.stream_id(synth.KIND_PREFIX_MAP), idx, P)
+    th = np.where(idx < P, pth[np.minimum(idx, P - 1)], host_master(w, sh.lo + idx)).astype(np.float32)
+    m, v = pm[src].copy(), pv[src].copy()
+    parts = host_partials(w, t0, sh.lo + idx)     # the bench reuses step t0's partials
+    for t in steps:
+        th, m, v, p = oracle.shard_step(parts, th, m, v, oracle.hparams(t, **w.hparams()))
+    check_state(gather_state(sh, idx), (th, m, v, p), "7b sampled")
+    del sh
+    release()
+
+
+def test_llama70b_sampled_two_steps(bench):
+    w = W.llama70b()
+    say(f"case: {w.name} rank 5 slot, 2 steps, sampled compare (shard {w.shard_len})")
+    sh = bench.Shard(w, rank=5)
+    assert sh.n > (1 << 32)
+    t0 = sh.prepare()
+    sh.step(t0)
+    sh.step(t0 + 1)
+    idx = sample_indices(sh.table, sh.n, seed=70)
+    idx = np.unique(np.concatenate([idx, np.array([(1 << 32) - 1, 1 << 32, (1 << 32) + 7])]))
+    say(f"  {idx.size} sampled indices")
+    th = host_master(w, sh.lo + idx)
+    m = np.zeros(idx.size, np.float32)
+    v = np.zeros(idx.size, np.float32)
+    parts = host_partials(w, t0, sh.lo + idx)
+    for t in (t0, t0 + 1):
+        th, m, v, p = oracle.shard_step(parts, th, m, v, oracle.hparams(t, **w.hparams()))
+    check_state(gather_state(sh, idx), (th, m, v, p), "70b sampled")
+    del sh
+    release()
