@@ -58,12 +58,13 @@ class Shard:
     """Device buffers of one rank's shard step for a workload."""
 
     def __init__(self, w: W.Workload, rank: int = 0, dst_mode: str = None,
-                 max_chunk: int = 65536, device: str = "cuda"):
+                 max_chunk: int = None, device: str = "cuda"):
         import torch
         import sharded_optimizer_step_shard_amd as zs
 
         self.w, self.rank, self.zs = w, rank, zs
         self.dst_mode = dst_mode or default_dst_mode(w)
+        max_chunk = max_chunk or zs.ZERO_DEFAULT_MAX_CHUNK
         self.lo, self.hi = w.shard_range(rank)
         self.n = self.hi - self.lo
         self.S = w.shard_len
@@ -122,7 +123,7 @@ class Shard:
         assert 0 < P <= self.n and P % 64 == 0
         # Prefix steps write their bf16 parameters into a scratch slot.
         scratch = torch.empty(P, dtype=torch.int16, device=self.dev)
-        table, _ = self.zs.zero_build_chunks([P], 1, 0, slot_dst=scratch, max_chunk=4096)
+        table, _ = self.zs.zero_build_chunks([P], 1, 0, slot_dst=scratch)
         d_table = self.zs.chunks_to_device(table, self.dev)
         for t in range(1, w.warm_steps + 1):
             self.fill_partials(t, count=P)
@@ -221,7 +222,8 @@ def main() -> int:
     ap.add_argument("--workload", default="llama7b", choices=sorted(W.ALL))
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--dst", default=None, choices=["slot", "tensors"])
-    ap.add_argument("--max-chunk", type=int, default=65536)
+    ap.add_argument("--max-chunk", type=int, default=None,
+                    help="chunk-table cut length (default: the library's tuned value)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()

@@ -112,7 +112,7 @@ enum {
 };
 
 #define ZERO_MAX_RANKS 64
-#define ZERO_DEFAULT_MAX_CHUNK 65536
+#define ZERO_DEFAULT_MAX_CHUNK 2048   /* chunk length the step kernel is tuned for */
 
 /*
  * Shard geometry and the chunk table (host only; no device calls).

@@ -234,8 +234,9 @@ int zero_shard_step(const void *const *partials, int n_ranks, zero_dtype gdt,
     a.m = m;
     a.v = v;
     a.chunks = d_chunks;
+    a.n_chunks = n_chunks;
     a.shard_len = shard_len;
-    return hip_status(launch_step(a, gdt, n_chunks, stream));
+    return hip_status(launch_step(a, gdt, stream));
 }
 
 int zero_reduce_shard(const void *const *partials, int n_ranks, zero_dtype gdt, int64_t n,
@@ -307,8 +308,9 @@ int zero_gather_write(const float *master, int64_t shard_len, const zero_chunk *
     GatherArgs a;
     a.master = master;
     a.chunks = d_chunks;
+    a.n_chunks = n_chunks;
     a.shard_len = shard_len;
-    return hip_status(launch_gather(a, n_chunks, stream));
+    return hip_status(launch_gather(a, stream));
 }
 
 int zero_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream)

@@ -38,6 +38,7 @@ struct StepArgs {
     StepScalars k;
     float *master, *m, *v;
     const zero_chunk *chunks;
+    int64_t n_chunks;
     int64_t shard_len;
 };
 
@@ -58,13 +59,14 @@ struct AdamArgs {
 struct GatherArgs {
     const float *master;
     const zero_chunk *chunks;
+    int64_t n_chunks;
     int64_t shard_len;
 };
 
-hipError_t launch_step(const StepArgs &a, zero_dtype gdt, int64_t n_chunks, hipStream_t s);
+hipError_t launch_step(const StepArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs &a, hipStream_t s);
-hipError_t launch_gather(const GatherArgs &a, int64_t n_chunks, hipStream_t s);
+hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s);
 
 }  // namespace zs

@@ -8,10 +8,12 @@
 // so no MFMA; the kernels are built around 16-byte per-lane accesses that
 // a wave turns into fully coalesced 1 KiB requests.
 //
-// Work split: one workgroup (256 lanes, 4 waves) per chunk of the chunk
-// table.  A lane handles a group of VEC consecutive elements (8 with bf16
-// partials: one 16-byte load per partial; 4 with fp32 partials), strided by
-// the workgroup size.  Groups sit on the shard's VEC-element grid, so all
+// Work split: one workgroup (a single wave of 64 lanes) per chunk of the
+// chunk table (a workgroup loops over chunks when the table is longer than
+// the grid cap).  A lane handles a group of VEC consecutive elements (8
+// with bf16 partials: one 16-byte load per partial; 4 with fp32 partials),
+// strided by the wave width; the default 2048-element chunk is four groups
+// per lane.  Groups sit on the shard's VEC-element grid, so all
 // partial and state loads are 16-byte aligned; a chunk that starts or ends
 // off the grid handles its first or last group element by element.
 //
@@ -20,13 +22,15 @@
 // library is built with -ffp-contract=off), one rounding per stored value.
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "zero_internal.h"
 
 namespace zs {
 
-constexpr int kBlock = 256;
+constexpr int kBlock = 256;       // grid-stride kernels (unfused, probe)
+constexpr int kStepBlock = 64;    // chunk-table kernels: one wave per workgroup
 
 // Native clang vectors: 16-byte (and 8-byte) loads and stores, and the
 // non-temporal store builtin, need them rather than HIP's struct wrappers.
@@ -78,6 +82,24 @@ __device__ __forceinline__ void adamw(float g32, float &th, float &m, float &v, 
 
 template <typename T>
 __device__ __forceinline__ T ld(const T *p) { return *p; }
+
+// The chunk table is read-only for the whole launch; reading it through the
+// constant address space lets the compiler use scalar loads for the
+// (uniform) descriptor instead of one vector load per lane.
+typedef __attribute__((address_space(4))) const int64_t const_i64;
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+__device__ __forceinline__ zero_chunk chunk_at(const zero_chunk *table, int64_t ci)
+{
+    const char *p = (const char *)(table + __builtin_amdgcn_readfirstlane((int)ci));
+    zero_chunk c;
+    c.shard_off = *(const_i64 *)(p + offsetof(zero_chunk, shard_off));
+    c.dst = (uint16_t *)(uintptr_t)*(const_i64 *)(p + offsetof(zero_chunk, dst));
+    c.len = *(const_i32 *)(p + offsetof(zero_chunk, len));
+    c.tensor_id = *(const_i32 *)(p + offsetof(zero_chunk, tensor_id));
+    c.tensor_off = *(const_i64 *)(p + offsetof(zero_chunk, tensor_off));
+    return c;
+}
 
 template <typename T>
 __device__ __forceinline__ void st_nt(T *p, T x) { __builtin_nontemporal_store(x, p); }
@@ -146,6 +168,9 @@ __device__ __forceinline__ void group_sum(double *s, const PartialPtrs &pp, int 
 #pragma unroll
             for (int j = 0; j < B; ++j)
                 raw[j] = ld_raw(pp.p[kb + j], off);
+            // Keep the batch's loads (and any issued before them) ahead of
+            // the arithmetic: a stream kernel wants every request in flight.
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < B; ++j) {
                 if (kb + j == 0)
@@ -217,10 +242,9 @@ __device__ __forceinline__ void store_bf16(uint16_t *dst, const uint32_t *h, boo
 // ---------------------------------------------------------------- fused step
 
 template <zero_dtype G, int NC>
-__global__ __launch_bounds__(kBlock) void shard_step_kernel(StepArgs a)
+__device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &c)
 {
     constexpr int VEC = Grad<G>::VEC;
-    const zero_chunk c = a.chunks[blockIdx.x];
     if (c.len <= 0 || c.shard_off < 0 || c.shard_off > a.shard_len - c.len)
         return;
     const int n = NC > 0 ? NC : a.red.n_ranks;
@@ -229,16 +253,16 @@ __global__ __launch_bounds__(kBlock) void shard_step_kernel(StepArgs a)
     // dst address of the first element of group g0, aligned for a vector store?
     const bool vec_ok = (((uintptr_t)c.dst - (uintptr_t)(2 * (lo - g0 * VEC))) % (2 * VEC)) == 0;
 
-    for (int64_t g = g0 + threadIdx.x; g < g1; g += kBlock) {
+    for (int64_t g = g0 + threadIdx.x; g < g1; g += kStepBlock) {
         const int64_t i0 = g * VEC;
         uint16_t *d = c.dst + (i0 - lo);
         if (i0 >= lo && i0 + VEC <= hi) {
             double s[VEC];
-            group_sum<G, NC>(s, a.parts, n, i0);
             F32x<VEC> th, m, v;
             th.load(a.master + i0);
             m.load(a.m + i0);
             v.load(a.v + i0);
+            group_sum<G, NC>(s, a.parts, n, i0);
             uint32_t h[VEC];
 #pragma unroll
             for (int j = 0; j < VEC; ++j) {
@@ -265,6 +289,21 @@ __global__ __launch_bounds__(kBlock) void shard_step_kernel(StepArgs a)
             }
         }
     }
+}
+
+// A workgroup (one wave) takes chunks blockIdx.x, blockIdx.x + gridDim.x,
+// ...: the grid is capped so that work-items stay below 2^32 however long
+// the table is.  At most one wave per SIMD (waves_per_eu): with fewer
+// concurrent streams the HBM sustains more of its peak on this mixed
+// read/write stream, measured across chunk sizes and block shapes on
+// MI355X (4 resident waves per CU beat 8-16).  Each wave still keeps its
+// group's 14 (N = 8) to 22 (N = 16) 16-byte loads in flight at once.
+template <zero_dtype G, int NC>
+__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void shard_step_kernel(StepArgs a)
+{
+    for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
+        step_chunk<G, NC>(a, chunk_at(a.chunks, ci));
 }
 
 // ---------------------------------------------------------------- unfused
@@ -323,16 +362,15 @@ __global__ __launch_bounds__(kBlock) void adamw_kernel(AdamArgs a)
     }
 }
 
-__global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
+__device__ __forceinline__ void gather_chunk(const GatherArgs &a, const zero_chunk &c)
 {
     constexpr int VEC = 8;
-    const zero_chunk c = a.chunks[blockIdx.x];
     if (c.len <= 0 || c.shard_off < 0 || c.shard_off > a.shard_len - c.len)
         return;
     const int64_t lo = c.shard_off, hi = c.shard_off + c.len;
     const int64_t g0 = lo / VEC, g1 = (hi + VEC - 1) / VEC;
     const bool vec_ok = (((uintptr_t)c.dst - (uintptr_t)(2 * (lo - g0 * VEC))) % (2 * VEC)) == 0;
-    for (int64_t g = g0 + threadIdx.x; g < g1; g += kBlock) {
+    for (int64_t g = g0 + threadIdx.x; g < g1; g += kStepBlock) {
         const int64_t i0 = g * VEC;
         uint16_t *d = c.dst + (i0 - lo);
         if (i0 >= lo && i0 + VEC <= hi) {
@@ -351,6 +389,13 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
             }
         }
     }
+}
+
+__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gather_kernel(GatherArgs a)
+{
+    for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
+        gather_chunk(a, chunk_at(a.chunks, ci));
 }
 
 __global__ __launch_bounds__(kBlock) void probe_copy_kernel(const u32x4 *src, u32x4 *dst, int64_t n16,
@@ -377,10 +422,19 @@ static int grid_for(int64_t items)
     return blocks < 1 ? 1 : (int)blocks;
 }
 
-template <zero_dtype G>
-static hipError_t step_dispatch(const StepArgs &a, int64_t n_chunks, hipStream_t s)
+// Chunk-table launches: one workgroup per chunk up to kMaxChunkGrid
+// workgroups (kMaxChunkGrid * kStepBlock < 2^32 work-items).
+constexpr int64_t kMaxChunkGrid = int64_t(1) << 22;
+
+static unsigned chunk_grid(int64_t n_chunks)
 {
-    dim3 grid((unsigned)n_chunks), block(kBlock);
+    return (unsigned)(n_chunks < kMaxChunkGrid ? n_chunks : kMaxChunkGrid);
+}
+
+template <zero_dtype G>
+static hipError_t step_dispatch(const StepArgs &a, hipStream_t s)
+{
+    dim3 grid(chunk_grid(a.n_chunks)), block(kStepBlock);
     switch (a.red.n_ranks) {
     case 1: hipLaunchKernelGGL((shard_step_kernel<G, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((shard_step_kernel<G, 2>), grid, block, 0, s, a); break;
@@ -394,10 +448,9 @@ static hipError_t step_dispatch(const StepArgs &a, int64_t n_chunks, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t launch_step(const StepArgs &a, zero_dtype gdt, int64_t n_chunks, hipStream_t s)
+hipError_t launch_step(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 {
-    return gdt == ZERO_BF16 ? step_dispatch<ZERO_BF16>(a, n_chunks, s)
-                            : step_dispatch<ZERO_FP32>(a, n_chunks, s);
+    return gdt == ZERO_BF16 ? step_dispatch<ZERO_BF16>(a, s) : step_dispatch<ZERO_FP32>(a, s);
 }
 
 template <zero_dtype G>
@@ -428,9 +481,9 @@ hipError_t launch_adamw(const AdamArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_gather(const GatherArgs &a, int64_t n_chunks, hipStream_t s)
+hipError_t launch_gather(const GatherArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)n_chunks), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(gather_kernel, dim3(chunk_grid(a.n_chunks)), dim3(kStepBlock), 0, s, a);
     return hipGetLastError();
 }
 
