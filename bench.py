@@ -202,6 +202,31 @@ def cpu_baseline(w: W.Workload, rank: int, t: int, target_s: float = 10.0,
                       f"{w.gdt} partials, {reps} oracle steps in {elapsed:.1f} s"}
 
 
+def probe_copy(nbytes: int, reps: int = 5) -> dict:
+    """Plain device-to-device copy of nbytes (read nbytes + write nbytes)
+    with zero_probe_copy: the attainable streaming rate next to the step's."""
+    import torch
+    import sharded_optimizer_step_shard_amd as zs
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    zs.zero_probe_copy(src, dst, nbytes)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        zs.zero_probe_copy(src, dst, nbytes)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_copied": nbytes, "ms": ms, "gbs": 2 * nbytes / (ms * 1e-3) / 1e9,
+            "frac_of_peak": 2 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def load_traffic(kernel_key: str) -> dict:
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
@@ -225,6 +250,10 @@ def main() -> int:
     ap.add_argument("--max-chunk", type=int, default=None,
                     help="chunk-table cut length (default: the library's tuned value)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe-copy", type=int, default=1 << 32, metavar="BYTES",
+                    help="after timing, copy BYTES with the library's plain copy kernel "
+                         "(measured copy bandwidth of this GPU; the known-size kernel that "
+                         "calibrates HBM traffic counters); 0 to skip")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
 
@@ -290,6 +319,8 @@ def main() -> int:
                      "kernel": kernel_key, "kernel_ms": kernel_ms,
                      "algorithmic_bytes_per_launch": bytes_launch},
     }
+    if args.probe_copy > 0:
+        out["probe_copy"] = probe_copy(args.probe_copy)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.rank, t, args.cpu_seconds)
     print(json.dumps(out), flush=True)
