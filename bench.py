@@ -89,6 +89,7 @@ class Shard:
         self.table = table
         self.d_table = zs.chunks_to_device(table, dev)
         self.step_t = 0
+        self.buckets = [(0, len(table))]
         synth.dev_fill(self.master, w.seed, synth.stream_id(synth.KIND_MASTER), self.lo,
                        w.sigma_master)
 
@@ -153,6 +154,23 @@ class Shard:
                                 self.zs.hparams(t, **self.w.hparams()))
         self.step_t = t
 
+    def set_buckets(self, bucket_params: int) -> list:
+        """ZeRO-2 style buckets: split the chunk table into contiguous runs of
+        about bucket_params shard elements (whole chunks).  Each bucket is then
+        stepped by its own launch over its sub-table, as when each gradient
+        bucket's reduce-scatter completes separately.  Returns the
+        (first chunk, chunk count) runs."""
+        self.buckets = bucket_runs(self.table["len"], bucket_params)
+        return self.buckets
+
+    def step_bucketed(self, t: int) -> None:
+        hp = self.zs.hparams(t, **self.w.hparams())
+        base = self.d_table.data_ptr()
+        for first, count in self.buckets:
+            self.zs.zero_shard_step(self.partials, self.master, self.m, self.v, self.n,
+                                    base + 32 * first, count, hp)
+        self.step_t = t
+
     def param_at(self, shard_idx: np.ndarray):
         """bf16 bits written for the given shard indices (device gather)."""
         import torch
@@ -172,6 +190,25 @@ class Shard:
 
     def bytes_per_launch(self) -> int:
         return self.w.bytes_per_param() * self.n
+
+
+def bucket_runs(chunk_lens, bucket_params: int) -> list:
+    """Split a chunk table (its len column) into contiguous runs of whole
+    chunks holding at least bucket_params elements each (the last run may
+    hold fewer); returns (first chunk, chunk count) pairs covering every
+    chunk once, in order."""
+    lens = np.asarray(chunk_lens, dtype=np.int64)
+    if bucket_params <= 0:
+        raise ValueError("bucket_params must be positive")
+    ends = np.cumsum(lens)
+    runs, first = [], 0
+    while first < len(lens):
+        base = ends[first - 1] if first else 0
+        last = int(np.searchsorted(ends, base + bucket_params, side="left"))
+        last = min(max(last, first), len(lens) - 1)
+        runs.append((first, last - first + 1))
+        first = last + 1
+    return runs
 
 
 def cpu_baseline(w: W.Workload, rank: int, t: int, target_s: float = 10.0,
@@ -250,6 +287,9 @@ def main() -> int:
     ap.add_argument("--max-chunk", type=int, default=None,
                     help="chunk-table cut length (default: the library's tuned value)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bucket-params", type=int, default=0,
+                    help="step the shard in buckets of about this many params, one launch "
+                         "per bucket (ZeRO-2 bucketed step); 0 = one launch per step")
     ap.add_argument("--probe-copy", type=int, default=1 << 32, metavar="BYTES",
                     help="after timing, copy BYTES with the library's plain copy kernel "
                          "(measured copy bandwidth of this GPU; the known-size kernel that "
@@ -272,8 +312,12 @@ def main() -> int:
     print(f"# {w.name}: shard {sh.n} params, N={w.n_ranks} {w.gdt}, {len(sh.table)} chunks, "
           f"dst={sh.dst_mode}, first timed step t={t + args.warmup}", file=sys.stderr, flush=True)
 
+    step = sh.step
+    if args.bucket_params > 0:
+        sh.set_buckets(args.bucket_params)
+        step = sh.step_bucketed
     for _ in range(args.warmup):
-        sh.step(t)
+        step(t)
         t += 1
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -282,18 +326,19 @@ def main() -> int:
     wall0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        sh.step(t)
+        step(t)
         t += 1
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps   # one launch per step
+    launches = len(sh.buckets) if args.bucket_params > 0 else 1
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps / launches   # average launch
     ms_per_step = wall * 1e3 / args.steps
 
-    bytes_launch = sh.bytes_per_launch()
+    bytes_launch = sh.bytes_per_launch() / launches
     achieved = bytes_launch / (kernel_ms * 1e-3) / 1e9
     kernel_key = f"shard_step_kernel<{w.gdt},{w.n_ranks}>/{w.name}"
-    traffic = load_traffic(kernel_key)
+    traffic = load_traffic(kernel_key) if launches == 1 else None
     out = {
         "metric": "params updated/sec and achieved HBM GB/s (fraction of peak), fused shard step",
         "value": sh.n / (ms_per_step * 1e-3),
@@ -311,6 +356,7 @@ def main() -> int:
                    "n_ranks": w.n_ranks, "grad_dtype": w.gdt, "state_dtype": "fp32",
                    "param_dtype": "bf16", "tensors": len(w.numels), "chunks": len(sh.table),
                    "dst": sh.dst_mode, "bytes_per_param": w.bytes_per_param(),
+                   "launches_per_step": launches,
                    "parallelism": "one data-parallel rank's ZeRO shard"},
         "hbm_gbs": achieved,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -135,3 +135,28 @@ def test_llama70b_sampled_two_steps(bench):
     check_state(gather_state(sh, idx), (th, m, v, p), "70b sampled")
     del sh
     release()
+
+
+@pytest.mark.parametrize("bucket_params", [1 << 20, 3_000_000])
+def test_gpt2_bucketed_step_equals_oracle(bench, bucket_params):
+    """ZeRO-2 bucketed step: one launch per bucket (a contiguous run of the
+    chunk table) gives the same bits as the oracle's whole-shard step."""
+    w = W.gpt2()
+    say(f"case: {w.name} rank 1, buckets of ~{bucket_params} params, 3 steps")
+    sh = bench.Shard(w, rank=1)
+    runs = sh.set_buckets(bucket_params)
+    assert len(runs) > 1
+    idx = np.arange(sh.lo, sh.hi, dtype=np.int64)
+    th = host_master(w, idx)
+    m = np.zeros(sh.n, np.float32)
+    v = np.zeros(sh.n, np.float32)
+    for t in (1, 2, 3):
+        sh.fill_partials(t)
+        sh.step_bucketed(t)
+        th, m, v, p = oracle.shard_step(host_partials(w, t, idx), th, m, v,
+                                        oracle.hparams(t, **w.hparams()))
+    flat = np.concatenate([host(x) for x in sh.params])
+    check_state((host(sh.master), host(sh.m), host(sh.v), flat[sh.lo:sh.hi]), (th, m, v, p),
+                f"gpt2 bucketed {bucket_params}")
+    del sh
+    release()
