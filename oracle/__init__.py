@@ -50,12 +50,17 @@ def _load(path: str):
     L.oracle_adamw.argtypes = [vp, vp, vp, vp, i64, ctypes.POINTER(HParams)]
     L.oracle_shard_step.argtypes = [vp, i32, i32, i64, vp, vp, vp,
                                     ctypes.POINTER(HParams), vp]
+    L.oracle_reduce_ex.argtypes = [vp, i32, i32, i32, vp, i64, i64, vp]
+    L.oracle_accumulate.argtypes = [vp, i32, i32, i32, i64, vp, i32]
+    L.oracle_shard_step_ex.argtypes = [vp, i32, i32, i32, vp, i64, i64, vp, vp, vp,
+                                       ctypes.POINTER(HParams), vp]
     L.oracle_shard_segments.argtypes = [vp, i32, i32, i32, vp, i64, ctypes.POINTER(i64)]
     L.oracle_shard_segments.restype = i64
     L.oracle_set_threads.argtypes = [i32]
     L.oracle_max_threads.restype = i32
     for f in (L.oracle_bf16_round_array, L.oracle_reduce, L.oracle_adamw,
-              L.oracle_shard_step, L.oracle_set_threads):
+              L.oracle_shard_step, L.oracle_set_threads, L.oracle_reduce_ex,
+              L.oracle_accumulate, L.oracle_shard_step_ex):
         f.restype = None
     return L
 
@@ -141,6 +146,46 @@ def shard_step(partials: Sequence[np.ndarray], master: np.ndarray, m: np.ndarray
     prm = np.empty(n, dtype=np.uint16)
     lib().oracle_shard_step(_ptr_array(partials), len(partials), _gdt(partials), n,
                             _p(th), _p(mm), _p(vv), ctypes.byref(hp), _p(prm))
+    return th, mm, vv, prm
+
+
+def _group_of(n_ranks: int, group) -> int:
+    g = n_ranks if group in (None, 0) else int(group)
+    assert 1 <= g <= n_ranks and n_ranks % g == 0, "group must divide the rank count"
+    return g
+
+
+def reduce_ex(partials: Sequence[np.ndarray], group=None, acc=None,
+              micro_batches: int = 1) -> np.ndarray:
+    """fp32(((acc +) grouped sum) / (N * micro_batches)); group = ranks per
+    group of the two-level order (None: one group, the flat order)."""
+    n = partials[0].size
+    out = np.empty(n, dtype=np.float32)
+    a = None if acc is None else np.ascontiguousarray(acc, dtype=np.float32)
+    lib().oracle_reduce_ex(_ptr_array(partials), len(partials), _group_of(len(partials), group),
+                           _gdt(partials), None if a is None else _p(a), micro_batches, n, _p(out))
+    return out
+
+
+def accumulate(partials: Sequence[np.ndarray], acc=None, group=None) -> np.ndarray:
+    """One non-final micro-batch: new fp32 accumulator (acc None: start)."""
+    n = partials[0].size
+    out = np.zeros(n, np.float32) if acc is None else np.array(acc, dtype=np.float32, copy=True)
+    lib().oracle_accumulate(_ptr_array(partials), len(partials), _group_of(len(partials), group),
+                            _gdt(partials), n, _p(out), 1 if acc is None else 0)
+    return out
+
+
+def shard_step_ex(partials: Sequence[np.ndarray], master, m, v, hp: HParams, group=None,
+                  acc=None, micro_batches: int = 1):
+    """Shard step with the extended reduce; returns (master, m, v, param bits)."""
+    n = master.size
+    th, mm, vv = (np.array(x, dtype=np.float32, copy=True) for x in (master, m, v))
+    prm = np.empty(n, dtype=np.uint16)
+    a = None if acc is None else np.ascontiguousarray(acc, dtype=np.float32)
+    lib().oracle_shard_step_ex(_ptr_array(partials), len(partials), _group_of(len(partials), group),
+                               _gdt(partials), None if a is None else _p(a), micro_batches, n,
+                               _p(th), _p(mm), _p(vv), ctypes.byref(hp), _p(prm))
     return th, mm, vv, prm
 
 

@@ -139,6 +139,48 @@ static double bias_correction(double beta, int64_t t)
     return 1.0 - pow(beta, (double)t);
 }
 
+/*
+ * Two extensions of the reduce, for data-parallel layouts beyond one flat
+ * group and for more than one micro-batch per step:
+ *
+ *  - Hybrid sharding (CS231n "Large-Scale Distributed Training" notes, 4.4:
+ *    N = M x K GPUs, sharded inside each group of K, replicated across the
+ *    M groups).  The gradient is reduced inside each group first, then
+ *    across groups.  Order: ranks m*K .. m*K+K-1 form group m; each group's
+ *    partials are summed in rank order, then the M group sums in group
+ *    order, all in double.  K = N (one group) and K = 1 both give the flat
+ *    rank-order fold.
+ *
+ *  - Gradient accumulation over G micro-batches ("并行训练优化、MoE扩展与系统
+ *    瓶颈", 3.1: the effective batch is micro-batch x data-parallel size x
+ *    accumulation steps).  The gradient is the mean over all N x G
+ *    micro-batch gradients.  An fp32 accumulator holds the running sum of
+ *    the earlier micro-batches' reductions: after micro-batch j it is
+ *    fp32(acc + s_j) (for j = 0 just fp32(s_0)); the last micro-batch's
+ *    step uses g = fp32((acc + s_last) / (N G)), sums in double.
+ */
+static double grouped_sum(const void *const *partials, int n_ranks, int group, int gdt,
+                          int64_t i)
+{
+    double s = 0.0;
+    for (int m = 0; m < n_ranks / group; ++m) {
+        double t = partial_at(partials[m * group], gdt, i);
+        for (int k = 1; k < group; ++k)
+            t = t + partial_at(partials[m * group + k], gdt, i);
+        s = (m == 0) ? t : s + t;
+    }
+    return s;
+}
+
+static float reduce_ex_one(const void *const *partials, int n_ranks, int group, int gdt,
+                           const float *acc, int64_t micro_batches, int64_t i)
+{
+    double s = grouped_sum(partials, n_ranks, group, gdt, i);
+    if (acc)
+        s = (double)acc[i] + s;
+    return (float)(s / ((double)n_ranks * (double)micro_batches));
+}
+
 /* ---- array entry points --------------------------------------------- */
 
 /* g_out[i] = fp32( (p_0[i] + p_1[i] + ... + p_{N-1}[i]) / N ), i in [0, n). */
@@ -170,6 +212,42 @@ void oracle_shard_step(const void *const *partials, int n_ranks, int gdt, int64_
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         float g = reduce_one(partials, n_ranks, gdt, i);
+        adamw_one(g, &master[i], &m[i], &v[i], hp, bc1, bc2);
+        if (param_out)
+            param_out[i] = oracle_bf16_round(master[i]);
+    }
+}
+
+/* g_out[i] = fp32(((acc[i] if acc) + grouped sum) / (N * micro_batches)). */
+void oracle_reduce_ex(const void *const *partials, int n_ranks, int group, int gdt,
+                      const float *acc, int64_t micro_batches, int64_t n, float *g_out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        g_out[i] = reduce_ex_one(partials, n_ranks, group, gdt, acc, micro_batches, i);
+}
+
+/* One non-final micro-batch: acc[i] = fp32((reset ? 0 : acc[i]) + grouped sum). */
+void oracle_accumulate(const void *const *partials, int n_ranks, int group, int gdt,
+                       int64_t n, float *acc, int reset)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double s = grouped_sum(partials, n_ranks, group, gdt, i);
+        acc[i] = reset ? (float)s : (float)((double)acc[i] + s);
+    }
+}
+
+/* The whole shard step with the extended reduce. */
+void oracle_shard_step_ex(const void *const *partials, int n_ranks, int group, int gdt,
+                          const float *acc, int64_t micro_batches, int64_t n, float *master,
+                          float *m, float *v, const oracle_hparams *hp, uint16_t *param_out)
+{
+    double bc1 = bias_correction(hp->beta1, hp->step);
+    double bc2 = bias_correction(hp->beta2, hp->step);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float g = reduce_ex_one(partials, n_ranks, group, gdt, acc, micro_batches, i);
         adamw_one(g, &master[i], &m[i], &v[i], hp, bc1, bc2);
         if (param_out)
             param_out[i] = oracle_bf16_round(master[i]);

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import test_oracle_pins as pins
+import test_oracle_pins_ex as pins_ex
 
 MUTANTS = {
     "drop_last_rank": ("for (int k = 1; k < n_ranks; ++k)", "for (int k = 1; k < n_ranks - 1; ++k)"),
@@ -38,6 +39,17 @@ MUTANTS = {
     "bf16_truncate": ("hi = (uint16_t)(hi + 1u);", "hi = hi;"),
     "shard_len_floor": ("int64_t S = (total + n_ranks - 1) / n_ranks;", "int64_t S = total / n_ranks;"),
     "segment_offset": ("seg[4 * count + 1] = x - a;", "seg[4 * count + 1] = x - lo;"),
+    "group_transposed": ("t = t + partial_at(partials[m * group + k], gdt, i);",
+                         "t = t + partial_at(partials[k * (n_ranks / group) + m], gdt, i);"),
+    "group_head_transposed": ("double t = partial_at(partials[m * group], gdt, i);",
+                              "double t = partial_at(partials[m], gdt, i);"),
+    "grouped_flat_fold": ("        s = (m == 0) ? t : s + t;\n", "        s = s + t;\n"),
+    "acc_ignored": ("        s = (double)acc[i] + s;\n", "        s = s;\n"),
+    "divisor_ignores_micro_batches": ("(double)n_ranks * (double)micro_batches", "(double)n_ranks"),
+    "accumulate_reset_ignored": ("acc[i] = reset ? (float)s : (float)((double)acc[i] + s);",
+                                 "acc[i] = (float)((double)acc[i] + s);"),
+    "accumulate_rounds_twice": ("acc[i] = reset ? (float)s : (float)((double)acc[i] + s);",
+                                "acc[i] = reset ? (float)s : (float)((double)acc[i] + (double)(float)s);"),
 }
 
 FAST_PINS = [
@@ -52,6 +64,11 @@ FAST_PINS = [
     lambda: pins.test_adamw_zero_betas_reduce_to_normalised_step(),
     lambda: pins.test_adamw_constant_gradient_unbiased_moments(),
     lambda: [pins.test_shard_segments_brute_force(s) for s in range(6)],
+    lambda: pins_ex.test_one_group_and_singleton_groups_are_the_flat_order(8),
+    lambda: pins_ex.test_grouping_decides_the_rounding(),
+    lambda: pins_ex.test_grouped_mean_is_exact_when_sums_are_exact(8, 2),
+    lambda: pins_ex.test_accumulated_micro_batches_give_the_full_batch_gradient(2),
+    lambda: pins_ex.test_accumulator_rounds_once_per_micro_batch(),
 ]
 
 
