@@ -165,6 +165,53 @@ int zero_shard_step(const void *const *partials, int n_ranks, zero_dtype gdt,
                     const zero_adamw_hparams *hp, hipStream_t stream);
 
 /*
+ * Extended reduce for data-parallel layouts beyond one flat group and for
+ * more than one micro-batch per optimizer step.
+ *
+ * Two-level order (hybrid sharding, CS231n "Large-Scale Distributed
+ * Training" notes, 4.4: N = M x K GPUs, sharded inside each group of K,
+ * replicated across the M groups): partials m*K .. m*K+K-1 form group m;
+ * each group is summed in rank order, then the group sums in group order,
+ * all in double.  group = 0 or group = n_ranks is the flat order of
+ * zero_shard_step; group = 1 gives the same bits too.  The shard geometry
+ * then uses the K ranks of one group (zero_build_chunks with n_ranks = K),
+ * while n_ranks here counts all N partials.
+ *
+ * Gradient accumulation ("并行训练优化、MoE扩展与系统瓶颈", 3.1: the effective
+ * batch grows with the number of accumulation steps G): the gradient is the
+ * mean over all N x G micro-batch gradients.  Micro-batches 0 .. G-2 go
+ * through zero_accumulate_shard into an fp32 accumulator acc (after each,
+ * acc = fp32(acc + that micro-batch's sum)); the step for the last one uses
+ * g = fp32((acc + its sum) / (N G)).
+ */
+typedef struct zero_reduce_spec {
+    int32_t group;          /* ranks per group of the two-level order; 0 = one group */
+    int32_t micro_batches;  /* G >= 1 */
+    const float *acc;       /* device, shard_len fp32: sum of micro-batches 0..G-2; NULL iff G == 1 */
+} zero_reduce_spec;
+
+/*
+ * The fused shard step with the extended reduce: as zero_shard_step, with
+ * g = fp32(((acc[i] if acc) + two-level sum) / (n_ranks * micro_batches)).
+ * rs: host pointer.  Errors as zero_shard_step; INVALID also when group
+ * does not divide n_ranks, micro_batches < 1, or acc is given iff
+ * micro_batches == 1; ALIAS when acc overlaps master, m or v.
+ */
+int zero_shard_step_ex(const void *const *partials, int n_ranks, zero_dtype gdt,
+                       const zero_reduce_spec *rs, float *master, float *m, float *v,
+                       int64_t shard_len, const zero_chunk *d_chunks, int64_t n_chunks,
+                       const zero_adamw_hparams *hp, hipStream_t stream);
+
+/*
+ * One non-final micro-batch of gradient accumulation:
+ * acc[i] = fp32((reset ? 0 : acc[i]) + two-level sum of p_0[i] .. p_{N-1}[i]),
+ * i in [0, n); with reset the sum alone is rounded (a -0 sum stays -0).
+ * group as in zero_reduce_spec.  acc must not overlap a partial (ALIAS).
+ */
+int zero_accumulate_shard(const void *const *partials, int n_ranks, zero_dtype gdt, int group,
+                          int64_t n, float *acc, int reset, hipStream_t stream);
+
+/*
  * Reduce only: grad_out[i] = fp32((p_0[i] + ... + p_{N-1}[i]) / N),
  * i in [0, n), summed in double in rank order.  grad_out must not overlap
  * any partial (ALIAS).  n == 0 is a no-op.

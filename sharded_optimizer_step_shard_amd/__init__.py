@@ -47,6 +47,12 @@ def hparams(step: int, lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.99
     return HParams(lr, beta1, beta2, eps, weight_decay, step)
 
 
+class ReduceSpec(ctypes.Structure):
+    """Mirrors `zero_reduce_spec`."""
+    _fields_ = [("group", ctypes.c_int32), ("micro_batches", ctypes.c_int32),
+                ("acc", ctypes.c_void_p)]
+
+
 class ZeroShardError(RuntimeError):
     def __init__(self, code: int, fn: str):
         self.code = code
@@ -63,6 +69,9 @@ _lib.zero_build_chunks.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp, _
                                    ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
 _lib.zero_shard_step.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64,
                                  ctypes.POINTER(HParams), _vp]
+_lib.zero_shard_step_ex.argtypes = [_vp, _i32, _i32, ctypes.POINTER(ReduceSpec), _vp, _vp, _vp,
+                                    _i64, _vp, _i64, ctypes.POINTER(HParams), _vp]
+_lib.zero_accumulate_shard.argtypes = [_vp, _i32, _i32, _i32, _i64, _vp, _i32, _vp]
 _lib.zero_reduce_shard.argtypes = [_vp, _i32, _i32, _i64, _vp, _vp]
 _lib.zero_adamw_shard.argtypes = [_vp, _vp, _vp, _vp, _i64, ctypes.POINTER(HParams), _vp]
 _lib.zero_gather_write.argtypes = [_vp, _i64, _vp, _i64, _vp]
@@ -70,7 +79,8 @@ _lib.zero_probe_copy.argtypes = [_vp, _vp, _i64, _vp]
 _lib.zero_strerror.argtypes = [_i32]
 _lib.zero_strerror.restype = ctypes.c_char_p
 for _f in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
-           "zero_gather_write", "zero_probe_copy", "zero_version"):
+           "zero_gather_write", "zero_probe_copy", "zero_version", "zero_shard_step_ex",
+           "zero_accumulate_shard"):
     getattr(_lib, _f).restype = _i32
 
 Ptr = Union[int, "torch.Tensor", None]  # noqa: F821
@@ -169,6 +179,29 @@ def zero_shard_step(partials: Sequence[Ptr], master: Ptr, m: Ptr, v: Ptr, shard_
     _check(_lib.zero_shard_step(_partial_array(partials), len(partials), gdt, _addr(master),
                                 _addr(m), _addr(v), shard_len, _addr(d_chunks), n_chunks,
                                 ctypes.byref(hp), _stream(stream)), "zero_shard_step")
+
+
+def zero_shard_step_ex(partials: Sequence[Ptr], master: Ptr, m: Ptr, v: Ptr, shard_len: int,
+                       d_chunks: Ptr, n_chunks: int, hp: HParams, group: int = 0,
+                       micro_batches: int = 1, acc: Ptr = None, gdt: Optional[int] = None,
+                       stream=None) -> None:
+    """Fused step with the two-level reduce order and/or an accumulator of
+    earlier micro-batches (see zero_reduce_spec)."""
+    gdt = _gdt_of(partials) if gdt is None else gdt
+    rs = ReduceSpec(group, micro_batches, _addr(acc))
+    _check(_lib.zero_shard_step_ex(_partial_array(partials), len(partials), gdt, ctypes.byref(rs),
+                                   _addr(master), _addr(m), _addr(v), shard_len, _addr(d_chunks),
+                                   n_chunks, ctypes.byref(hp), _stream(stream)),
+           "zero_shard_step_ex")
+
+
+def zero_accumulate_shard(partials: Sequence[Ptr], n: int, acc: Ptr, reset: bool,
+                          group: int = 0, gdt: Optional[int] = None, stream=None) -> None:
+    """acc = fp32((reset ? 0 : acc) + two-level sum of the partials)."""
+    gdt = _gdt_of(partials) if gdt is None else gdt
+    _check(_lib.zero_accumulate_shard(_partial_array(partials), len(partials), gdt, group, n,
+                                      _addr(acc), 1 if reset else 0, _stream(stream)),
+           "zero_accumulate_shard")
 
 
 def zero_reduce_shard(partials: Sequence[Ptr], n: int, grad_out: Ptr,

@@ -1,6 +1,8 @@
 """Build libzero_shard.so (the HIP library behind include/zero_shard.h) in-tree.
 
-    python -m sharded_optimizer_step_shard_amd.build
+    python sharded_optimizer_step_shard_amd/build.py
+
+(run as a script: importing the package needs the library already built).
 
 compiles csrc/zero_kernels.hip and csrc/zero_api.cpp for gfx950 with hipcc.
 Flags that matter for the results:

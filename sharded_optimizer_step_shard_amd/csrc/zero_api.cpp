@@ -53,14 +53,31 @@ StepScalars make_scalars(const zero_adamw_hparams *hp)
     return k;
 }
 
-ReduceScalars make_reduce(int n_ranks)
+// count = N * micro_batches, the number of gradients the mean runs over.
+ReduceScalars make_reduce(int n_ranks, int group = 0, int64_t micro_batches = 1)
 {
     ReduceScalars r;
+    const int64_t count = (int64_t)n_ranks * micro_batches;
     r.n_ranks = n_ranks;
-    r.n = (double)n_ranks;
-    r.pow2 = (n_ranks & (n_ranks - 1)) == 0;
-    r.inv_n = 1.0 / r.n;   // exact when n_ranks is a power of two
+    r.group = group > 0 ? group : n_ranks;
+    r.n = (double)count;
+    r.pow2 = (count & (count - 1)) == 0;
+    r.inv_n = 1.0 / r.n;   // exact when the count is a power of two
     return r;
+}
+
+// Two-level order and accumulation arguments: group divides n_ranks
+// (0 = one group); micro_batches >= 1; acc given exactly when there are
+// earlier micro-batches.
+bool valid_reduce_spec(const zero_reduce_spec *rs, int n_ranks)
+{
+    if (!rs)
+        return false;
+    if (rs->group < 0 || rs->group > n_ranks || (rs->group > 0 && n_ranks % rs->group != 0))
+        return false;
+    if (rs->micro_batches < 1 || (int64_t)rs->micro_batches * n_ranks > (int64_t(1) << 40))
+        return false;
+    return (rs->micro_batches > 1) == (rs->acc != nullptr);
 }
 
 int elem_bytes(zero_dtype gdt) { return gdt == ZERO_BF16 ? 2 : 4; }
@@ -107,7 +124,7 @@ bool in_device_alloc(const void *p, int64_t bytes)
 
 extern "C" {
 
-int zero_version(void) { return (1 << 16) | 0; }
+int zero_version(void) { return (1 << 16) | 1; }
 
 const char *zero_strerror(int code)
 {
@@ -237,6 +254,82 @@ int zero_shard_step(const void *const *partials, int n_ranks, zero_dtype gdt,
     a.n_chunks = n_chunks;
     a.shard_len = shard_len;
     return hip_status(launch_step(a, gdt, stream));
+}
+
+int zero_shard_step_ex(const void *const *partials, int n_ranks, zero_dtype gdt,
+                       const zero_reduce_spec *rs, float *master, float *m, float *v,
+                       int64_t shard_len, const zero_chunk *d_chunks, int64_t n_chunks,
+                       const zero_adamw_hparams *hp, hipStream_t stream)
+{
+    StepArgs a;
+    int rc = check_partials(partials, n_ranks, gdt, shard_len, a.parts);
+    if (rc)
+        return rc;
+    if (((!master || !m || !v) && shard_len > 0) || shard_len < 0 || n_chunks < 0 ||
+        n_chunks > INT32_MAX || (n_chunks > 0 && !d_chunks) || !valid_hparams(hp) ||
+        !valid_reduce_spec(rs, n_ranks))
+        return ZERO_ERR_INVALID;
+    if (!aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(d_chunks) ||
+        !aligned16(rs->acc))
+        return ZERO_ERR_MISALIGNED;
+    const int64_t sb = shard_len * 4, gb = shard_len * elem_bytes(gdt);
+    if (overlaps(master, sb, m, sb) || overlaps(master, sb, v, sb) || overlaps(m, sb, v, sb))
+        return ZERO_ERR_ALIAS;
+    for (int k = 0; k < n_ranks; ++k)
+        if (overlaps(partials[k], gb, master, sb) || overlaps(partials[k], gb, m, sb) ||
+            overlaps(partials[k], gb, v, sb))
+            return ZERO_ERR_ALIAS;
+    if (rs->acc && (overlaps(rs->acc, sb, master, sb) || overlaps(rs->acc, sb, m, sb) ||
+                    overlaps(rs->acc, sb, v, sb)))
+        return ZERO_ERR_ALIAS;
+    if (n_chunks == 0 || shard_len == 0)
+        return ZERO_OK;
+    for (int k = 0; k < n_ranks; ++k)
+        if (!in_device_alloc(partials[k], gb))
+            return ZERO_ERR_NOT_DEVICE;
+    if (!in_device_alloc(master, sb) || !in_device_alloc(m, sb) || !in_device_alloc(v, sb) ||
+        !in_device_alloc(d_chunks, n_chunks * (int64_t)sizeof(zero_chunk)) ||
+        (rs->acc && !in_device_alloc(rs->acc, sb)))
+        return ZERO_ERR_NOT_DEVICE;
+    a.red = make_reduce(n_ranks, rs->group, rs->micro_batches);
+    a.k = make_scalars(hp);
+    a.master = master;
+    a.m = m;
+    a.v = v;
+    a.chunks = d_chunks;
+    a.n_chunks = n_chunks;
+    a.shard_len = shard_len;
+    a.acc = rs->acc;
+    return hip_status(launch_step_ex(a, gdt, stream));
+}
+
+int zero_accumulate_shard(const void *const *partials, int n_ranks, zero_dtype gdt, int group,
+                          int64_t n, float *acc, int reset, hipStream_t stream)
+{
+    AccArgs a;
+    int rc = check_partials(partials, n_ranks, gdt, n, a.parts);
+    if (rc)
+        return rc;
+    if ((!acc && n > 0) || n < 0 || group < 0 || group > n_ranks ||
+        (group > 0 && n_ranks % group != 0))
+        return ZERO_ERR_INVALID;
+    if (!aligned16(acc))
+        return ZERO_ERR_MISALIGNED;
+    for (int k = 0; k < n_ranks; ++k)
+        if (overlaps(partials[k], n * elem_bytes(gdt), acc, n * 4))
+            return ZERO_ERR_ALIAS;
+    if (n == 0)
+        return ZERO_OK;
+    for (int k = 0; k < n_ranks; ++k)
+        if (!in_device_alloc(partials[k], n * elem_bytes(gdt)))
+            return ZERO_ERR_NOT_DEVICE;
+    if (!in_device_alloc(acc, n * 4))
+        return ZERO_ERR_NOT_DEVICE;
+    a.red = make_reduce(n_ranks, group, 1);
+    a.acc = acc;
+    a.n = n;
+    a.reset = reset ? 1 : 0;
+    return hip_status(launch_accumulate(a, gdt, stream));
 }
 
 int zero_reduce_shard(const void *const *partials, int n_ranks, zero_dtype gdt, int64_t n,

@@ -19,13 +19,16 @@ struct StepScalars {
     double dec;        // 1 - lr * weight_decay
 };
 
-// Reduction constants: divide by N, or multiply by 1/N when N is a power
-// of two (exact scaling, so the same bits as the division).
+// Reduction constants: divide by the count (N, or N * micro-batches), or
+// multiply by its inverse when the count is a power of two (exact scaling,
+// so the same bits as the division).  group: ranks per group of the
+// two-level order (n_ranks for the flat order).
 struct ReduceScalars {
     double n;
     double inv_n;
     int pow2;
     int n_ranks;
+    int group;
 };
 
 struct PartialPtrs {
@@ -40,6 +43,7 @@ struct StepArgs {
     const zero_chunk *chunks;
     int64_t n_chunks;
     int64_t shard_len;
+    const float *acc;   // extended step: earlier micro-batches' sum, or null
 };
 
 struct ReduceArgs {
@@ -47,6 +51,14 @@ struct ReduceArgs {
     ReduceScalars red;
     float *out;
     int64_t n;
+};
+
+struct AccArgs {
+    PartialPtrs parts;
+    ReduceScalars red;
+    float *acc;
+    int64_t n;
+    int reset;
 };
 
 struct AdamArgs {
@@ -64,6 +76,8 @@ struct GatherArgs {
 };
 
 hipError_t launch_step(const StepArgs &a, zero_dtype gdt, hipStream_t s);
+hipError_t launch_step_ex(const StepArgs &a, zero_dtype gdt, hipStream_t s);
+hipError_t launch_accumulate(const AccArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs &a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);

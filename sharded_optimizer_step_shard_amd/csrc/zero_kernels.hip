@@ -196,6 +196,91 @@ __device__ __forceinline__ double elem_sum(const PartialPtrs &pp, int n, int64_t
     return s;
 }
 
+// Two-level order (hybrid sharding): ranks m*K .. m*K+K-1 form group m; the
+// partials of a group are folded in rank order into t, and the group sums
+// into s in group order.  K = n gives the flat fold.  K is uniform, so the
+// group-boundary tests are scalar branches.
+template <zero_dtype G, int VEC>
+__device__ __forceinline__ void fold_two_level(double *s, double *t, u32x4 raw, int k, int K)
+{
+    double x[VEC];
+    Grad<G>::first(x, raw);
+    if (k % K == 0) {
+        if (k == K) {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) s[j] = t[j];
+        } else if (k > K) {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) s[j] = s[j] + t[j];
+        }
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) t[j] = x[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) t[j] = t[j] + x[j];
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void fold_finish(double *s, const double *t, int n, int K)
+{
+    if (n == K) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) s[j] = t[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) s[j] = s[j] + t[j];
+    }
+}
+
+template <zero_dtype G, int NC>
+__device__ __forceinline__ void group_sum_two_level(double *s, const PartialPtrs &pp, int n_rt,
+                                                    int K, int64_t i0)
+{
+    using GT = Grad<G>;
+    constexpr int VEC = GT::VEC;
+    const int64_t off = i0 * GT::BYTES;
+    double t[VEC];
+    if constexpr (NC > 0) {
+        constexpr int B = NC < 16 ? NC : 16;
+#pragma unroll
+        for (int kb = 0; kb < NC; kb += B) {
+            u32x4 raw[B];
+#pragma unroll
+            for (int j = 0; j < B; ++j)
+                raw[j] = ld_raw(pp.p[kb + j], off);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < B; ++j)
+                fold_two_level<G, VEC>(s, t, raw[j], kb + j, K);
+        }
+        fold_finish<VEC>(s, t, NC, K);
+    } else {
+        for (int k = 0; k < n_rt; ++k)
+            fold_two_level<G, VEC>(s, t, ld_raw(pp.p[k], off), k, K);
+        fold_finish<VEC>(s, t, n_rt, K);
+    }
+}
+
+template <zero_dtype G>
+__device__ __forceinline__ double elem_sum_two_level(const PartialPtrs &pp, int n, int K, int64_t i)
+{
+    double s = 0.0, t = 0.0;
+    for (int k = 0; k < n; ++k) {
+        const double x = Grad<G>::one(pp.p[k], i);
+        if (k % K == 0) {
+            if (k == K)
+                s = t;
+            else if (k > K)
+                s = s + t;
+            t = x;
+        } else {
+            t = t + x;
+        }
+    }
+    return n == K ? t : s + t;
+}
+
 // VEC fp32 values (4 or 8) at a 16-byte aligned address, moved with
 // 16-byte loads and non-temporal 16-byte stores.
 template <int VEC> struct F32x {
@@ -241,7 +326,9 @@ __device__ __forceinline__ void store_bf16(uint16_t *dst, const uint32_t *h, boo
 
 // ---------------------------------------------------------------- fused step
 
-template <zero_dtype G, int NC>
+// EXT: the extended reduce of zero_shard_step_ex (two-level order, optional
+// accumulator of earlier micro-batches, divisor N * micro-batches).
+template <zero_dtype G, int NC, bool EXT>
 __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &c)
 {
     constexpr int VEC = Grad<G>::VEC;
@@ -262,11 +349,23 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
             th.load(a.master + i0);
             m.load(a.m + i0);
             v.load(a.v + i0);
-            group_sum<G, NC>(s, a.parts, n, i0);
+            if constexpr (EXT) {
+                F32x<VEC> acc;
+                if (a.acc)
+                    acc.load(a.acc + i0);
+                group_sum_two_level<G, NC>(s, a.parts, n, a.red.group, i0);
+                if (a.acc) {
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j)
+                        s[j] = (double)acc[j] + s[j];
+                }
+            } else {
+                group_sum<G, NC>(s, a.parts, n, i0);
+            }
             uint32_t h[VEC];
 #pragma unroll
             for (int j = 0; j < VEC; ++j) {
-                float gj = finish_reduce<NC>(s[j], a.red);
+                float gj = finish_reduce<EXT ? 0 : NC>(s[j], a.red);
                 adamw(gj, th[j], m[j], v[j], a.k);
                 h[j] = to_bf16(th[j]);
             }
@@ -279,7 +378,15 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
                 const int64_t i = i0 + j;
                 if (i < lo || i >= hi)
                     continue;
-                float gj = finish_reduce<NC>(elem_sum<G>(a.parts, n, i), a.red);
+                float gj;
+                if constexpr (EXT) {
+                    double e = elem_sum_two_level<G>(a.parts, n, a.red.group, i);
+                    if (a.acc)
+                        e = (double)a.acc[i] + e;
+                    gj = finish_reduce<0>(e, a.red);
+                } else {
+                    gj = finish_reduce<NC>(elem_sum<G>(a.parts, n, i), a.red);
+                }
                 float th = a.master[i], m = a.m[i], v = a.v[i];
                 adamw(gj, th, m, v, a.k);
                 a.master[i] = th;
@@ -298,12 +405,12 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
 // read/write stream, measured across chunk sizes and block shapes on
 // MI355X (4 resident waves per CU beat 8-16).  Each wave still keeps its
 // group's 14 (N = 8) to 22 (N = 16) 16-byte loads in flight at once.
-template <zero_dtype G, int NC>
+template <zero_dtype G, int NC, bool EXT>
 __global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void shard_step_kernel(StepArgs a)
 {
     for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
-        step_chunk<G, NC>(a, chunk_at(a.chunks, ci));
+        step_chunk<G, NC, EXT>(a, chunk_at(a.chunks, ci));
 }
 
 // ---------------------------------------------------------------- unfused
@@ -329,6 +436,35 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a)
         const int64_t i = groups * VEC + threadIdx.x;
         if (i < a.n)
             a.out[i] = finish_reduce<NC>(elem_sum<G>(a.parts, n, i), a.red);
+    }
+}
+
+// One non-final micro-batch: acc = fp32((reset ? 0 : acc) + two-level sum).
+template <zero_dtype G, int NC>
+__global__ __launch_bounds__(kBlock) void accumulate_kernel(AccArgs a)
+{
+    constexpr int VEC = Grad<G>::VEC;
+    const int n = NC > 0 ? NC : a.red.n_ranks;
+    const int64_t groups = a.n / VEC;
+    for (int64_t g = (int64_t)blockIdx.x * kBlock + threadIdx.x; g < groups;
+         g += (int64_t)gridDim.x * kBlock) {
+        const int64_t i0 = g * VEC;
+        F32x<VEC> acc;
+        if (!a.reset)
+            acc.load(a.acc + i0);
+        double s[VEC];
+        group_sum_two_level<G, NC>(s, a.parts, n, a.red.group, i0);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            acc[j] = a.reset ? (float)s[j] : (float)((double)acc[j] + s[j]);
+        acc.store(a.acc + i0);
+    }
+    if (blockIdx.x == 0) {
+        const int64_t i = groups * VEC + threadIdx.x;
+        if (i < a.n) {
+            const double e = elem_sum_two_level<G>(a.parts, n, a.red.group, i);
+            a.acc[i] = a.reset ? (float)e : (float)((double)a.acc[i] + e);
+        }
     }
 }
 
@@ -431,26 +567,56 @@ static unsigned chunk_grid(int64_t n_chunks)
     return (unsigned)(n_chunks < kMaxChunkGrid ? n_chunks : kMaxChunkGrid);
 }
 
-template <zero_dtype G>
+template <zero_dtype G, bool EXT>
 static hipError_t step_dispatch(const StepArgs &a, hipStream_t s)
 {
     dim3 grid(chunk_grid(a.n_chunks)), block(kStepBlock);
     switch (a.red.n_ranks) {
-    case 1: hipLaunchKernelGGL((shard_step_kernel<G, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((shard_step_kernel<G, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((shard_step_kernel<G, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((shard_step_kernel<G, 8>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((shard_step_kernel<G, 16>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((shard_step_kernel<G, 32>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((shard_step_kernel<G, 64>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((shard_step_kernel<G, 0>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((shard_step_kernel<G, 1, EXT>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((shard_step_kernel<G, 2, EXT>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((shard_step_kernel<G, 4, EXT>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((shard_step_kernel<G, 8, EXT>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((shard_step_kernel<G, 16, EXT>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((shard_step_kernel<G, 32, EXT>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((shard_step_kernel<G, 64, EXT>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((shard_step_kernel<G, 0, EXT>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_step(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 {
-    return gdt == ZERO_BF16 ? step_dispatch<ZERO_BF16>(a, s) : step_dispatch<ZERO_FP32>(a, s);
+    return gdt == ZERO_BF16 ? step_dispatch<ZERO_BF16, false>(a, s)
+                            : step_dispatch<ZERO_FP32, false>(a, s);
+}
+
+hipError_t launch_step_ex(const StepArgs &a, zero_dtype gdt, hipStream_t s)
+{
+    return gdt == ZERO_BF16 ? step_dispatch<ZERO_BF16, true>(a, s)
+                            : step_dispatch<ZERO_FP32, true>(a, s);
+}
+
+template <zero_dtype G>
+static hipError_t accumulate_dispatch(const AccArgs &a, hipStream_t s)
+{
+    dim3 grid(grid_for(a.n / Grad<G>::VEC + 1)), block(kBlock);
+    switch (a.red.n_ranks) {
+    case 1: hipLaunchKernelGGL((accumulate_kernel<G, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((accumulate_kernel<G, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((accumulate_kernel<G, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((accumulate_kernel<G, 8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((accumulate_kernel<G, 16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((accumulate_kernel<G, 32>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((accumulate_kernel<G, 64>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((accumulate_kernel<G, 0>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_accumulate(const AccArgs &a, zero_dtype gdt, hipStream_t s)
+{
+    return gdt == ZERO_BF16 ? accumulate_dispatch<ZERO_BF16>(a, s)
+                            : accumulate_dispatch<ZERO_FP32>(a, s);
 }
 
 template <zero_dtype G>

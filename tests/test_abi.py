@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(zs):
 
 
 def test_version_and_strerror(zs):
-    assert zs.zero_version() == (1, 0)
+    assert zs.zero_version() == (1, 1)
     for code in range(8):
         assert zs.zero_strerror(code) and zs.zero_strerror(code) != "unknown error code"
     assert zs.zero_strerror(99) == "unknown error code"
@@ -219,3 +219,35 @@ def test_binding_fails_loudly_without_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import sharded_optimizer_step_shard_amd"],
                        cwd=tmp_path, capture_output=True, text=True)
     assert r.returncode != 0 and "missing" in r.stderr
+
+
+def step_ex(zs, p, n_ranks, rs, master=BASE + (1 << 40), n=1000):
+    hp = zs.hparams(1)
+    return zs.raw_call("zero_shard_step_ex", p, n_ranks, 0, ctypes.byref(rs), master,
+                       master + (1 << 32), master + (2 << 32), n, BASE + (1 << 41), 1,
+                       ctypes.byref(hp), None)
+
+
+def test_extended_reduce_argument_errors(zs):
+    R = zs.ReduceSpec
+    acc = BASE + (3 << 40)
+    assert step_ex(zs, parts(4), 4, R(3, 1, None)) == zs.ZERO_ERR_INVALID       # 3 does not divide 4
+    assert step_ex(zs, parts(4), 4, R(8, 1, None)) == zs.ZERO_ERR_INVALID       # group > n_ranks
+    assert step_ex(zs, parts(4), 4, R(-1, 1, None)) == zs.ZERO_ERR_INVALID
+    assert step_ex(zs, parts(4), 4, R(2, 0, None)) == zs.ZERO_ERR_INVALID       # micro_batches < 1
+    assert step_ex(zs, parts(4), 4, R(2, 1, acc)) == zs.ZERO_ERR_INVALID        # acc with G == 1
+    assert step_ex(zs, parts(4), 4, R(2, 3, None)) == zs.ZERO_ERR_INVALID       # no acc with G > 1
+    assert step_ex(zs, parts(4), 4, R(2, 3, acc + 4)) == zs.ZERO_ERR_MISALIGNED
+    assert step_ex(zs, parts(4), 4, R(2, 3, BASE + (1 << 40) + 64)) == zs.ZERO_ERR_ALIAS
+    assert step_ex(zs, parts(4), 4, R(2, 3, acc)) == zs.ZERO_ERR_NOT_DEVICE
+    assert step_ex(zs, parts(4), 4, R(0, 1, None)) == zs.ZERO_ERR_NOT_DEVICE
+    rc = zs.raw_call("zero_shard_step_ex", parts(4), 4, 0, None, BASE, BASE, BASE, 10, BASE, 1,
+                     ctypes.byref(zs.hparams(1)), None)
+    assert rc == zs.ZERO_ERR_INVALID                                             # null spec
+    acc_call = lambda *a: zs.raw_call("zero_accumulate_shard", *a)  # noqa: E731
+    assert acc_call(parts(4), 4, 0, 3, 100, acc, 1, None) == zs.ZERO_ERR_INVALID
+    assert acc_call(parts(4), 4, 0, 2, 100, None, 1, None) == zs.ZERO_ERR_INVALID
+    assert acc_call(parts(4), 4, 0, 2, 100, acc + 8, 1, None) == zs.ZERO_ERR_MISALIGNED
+    assert acc_call(parts(4), 4, 0, 2, 100, BASE + 64, 1, None) == zs.ZERO_ERR_ALIAS
+    assert acc_call(parts(4), 4, 0, 2, 100, acc, 0, None) == zs.ZERO_ERR_NOT_DEVICE
+    assert acc_call((ctypes.c_void_p * 4)(), 4, 0, 2, 0, None, 1, None) == zs.ZERO_OK

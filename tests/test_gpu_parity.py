@@ -233,3 +233,86 @@ def test_bf16_rounding_exhaustive(zs):
         u = np.arange(c << 28, (c + 1) << 28, dtype=np.uint64).astype(np.uint32)
         want = oracle.bf16_round(u.view(np.float32))
         assert_bitwise(host(out), want, f"bf16 block {c}", strict_nan=True)
+
+
+# ------------------------------------------------------------ extended reduce
+
+def _ext_case(zs, n_ranks, group, G, gdt, total=70_001, rank=0, max_chunk=192, steps=2):
+    """G micro-batches per step: G - 1 through zero_accumulate_shard, the last
+    through zero_shard_step_ex, against oracle.accumulate / shard_step_ex."""
+    w = W.Workload("ext", 95, [total], n_ranks, gdt, 1e-3)
+    S = -(-total // n_ranks)
+    lo, hi = min(rank * S, total), min((rank + 1) * S, total)
+    n = hi - lo
+    idx = np.arange(lo, hi, dtype=np.int64)
+    th_h = host_master(w, idx)
+    m_h = np.zeros(n, np.float32)
+    v_h = np.zeros(n, np.float32)
+    full = torch.full((total,), -1, dtype=torch.int16, device="cuda")
+    master, m, v = dev(th_h), dev(m_h), dev(v_h)
+    acc = torch.empty(max(n, 1), dtype=torch.float32, device="cuda")
+    table, _ = zs.zero_build_chunks([total], n_ranks, rank, slot_dst=full.data_ptr() + 2 * lo,
+                                    max_chunk=max_chunk)
+    d_table = zs.chunks_to_device(table)
+    for t in range(1, steps + 1):
+        acc_h = None
+        for j in range(G):
+            parts_h = host_partials(w, 100 * t + j, idx)
+            parts = [dev_bf16(p) if gdt == "bf16" else dev(p) for p in parts_h]
+            if j < G - 1:
+                zs.zero_accumulate_shard(parts, n, acc, reset=(j == 0), group=group)
+                acc_h = oracle.accumulate(parts_h, acc_h, group=group or None)
+                assert_bitwise(host(acc)[:n], acc_h, f"accumulator N={n_ranks} K={group} j={j}")
+            else:
+                zs.zero_shard_step_ex(parts, master, m, v, n, d_table, len(table), zs.hparams(t, **HP),
+                                      group=group, micro_batches=G, acc=acc if G > 1 else None)
+                th_h, m_h, v_h, p_h = oracle.shard_step_ex(parts_h, th_h, m_h, v_h, oracle.hparams(t, **HP),
+                                                           group=group or None, acc=acc_h, micro_batches=G)
+        fb = host(full)
+        check_state((host(master), host(m), host(v), fb[lo:hi]), (th_h, m_h, v_h, p_h),
+                    f"ext N={n_ranks} K={group} G={G} {gdt} step {t}")
+
+
+@pytest.mark.parametrize("n_ranks,group,G,gdt", [
+    (8, 0, 1, "bf16"), (8, 4, 1, "bf16"), (8, 2, 3, "bf16"), (8, 1, 2, "f32"),
+    (16, 8, 1, "bf16"), (16, 4, 4, "bf16"), (32, 8, 2, "f32"), (6, 3, 3, "bf16"),
+    (12, 4, 2, "f32"), (4, 2, 5, "bf16")])
+def test_extended_reduce_two_level_and_accumulation(zs, n_ranks, group, G, gdt):
+    say(f"case: extended reduce N={n_ranks} K={group} G={G} {gdt}")
+    _ext_case(zs, n_ranks, group, G, gdt, rank=n_ranks - 1)
+
+
+def test_extended_flat_equals_plain_step(zs):
+    """group 0, one micro-batch: the extended kernel gives the bits of the
+    plain fused kernel."""
+    say("case: extended flat vs plain step")
+    n, n_ranks = 50_003, 8
+    w = W.Workload("ef", 94, [n], n_ranks, "bf16", 1e-3)
+    idx = np.arange(n, dtype=np.int64)
+    parts = [dev_bf16(p) for p in host_partials(w, 1, idx)]
+    th = host_master(w, idx)
+    a = [dev(th), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")]
+    b = [dev(th), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")]
+    pa = torch.empty(n, dtype=torch.int16, device="cuda")
+    pb = torch.empty(n, dtype=torch.int16, device="cuda")
+    ta, _ = zs.zero_build_chunks([n], 1, 0, slot_dst=pa)
+    tb, _ = zs.zero_build_chunks([n], 1, 0, slot_dst=pb)
+    for t in (1, 2):
+        zs.zero_shard_step(parts, *a, n, zs.chunks_to_device(ta), len(ta), zs.hparams(t, **HP))
+        zs.zero_shard_step_ex(parts, *b, n, zs.chunks_to_device(tb), len(tb), zs.hparams(t, **HP))
+    for x, y, name in zip(a + [pa], b + [pb], ("master", "m", "v", "param")):
+        assert_bitwise(host(x), host(y), f"flat ex vs plain {name}")
+
+
+def test_grouping_decides_the_rounding_on_gpu(zs):
+    """The hand-derived case of the oracle pins: 2^60, 1, -2^60, 1 gives 0 with
+    two groups of two and 1/4 flat, through the GPU reduce."""
+    say("case: grouping rounding case on the GPU")
+    big = 2.0 ** 60
+    vals = [np.full(16, v, np.float32) for v in (big, 1.0, -big, 1.0)]
+    parts = [dev(x) for x in vals]
+    acc = torch.empty(16, dtype=torch.float32, device="cuda")
+    zs.zero_accumulate_shard(parts, 16, acc, reset=True, group=2)
+    assert np.all(host(acc) == 0.0)
+    zs.zero_accumulate_shard(parts, 16, acc, reset=True, group=0)
+    assert np.all(host(acc) == 1.0)
