@@ -154,6 +154,25 @@ class Shard:
                                 self.zs.hparams(t, **self.w.hparams()))
         self.step_t = t
 
+    def set_extended(self, group: int, micro_batches: int) -> None:
+        """Use the extended reduce: two-level order with `group` ranks per
+        group, and gradient accumulation over `micro_batches` (the same
+        partial buffers stand for every micro-batch)."""
+        import torch
+        self.group, self.micro_batches = group, micro_batches
+        self.acc = (torch.empty(self.n, dtype=torch.float32, device=self.dev)
+                    if micro_batches > 1 else None)
+
+    def step_extended(self, t: int) -> None:
+        for j in range(self.micro_batches - 1):
+            self.zs.zero_accumulate_shard(self.partials, self.n, self.acc, reset=(j == 0),
+                                          group=self.group)
+        self.zs.zero_shard_step_ex(self.partials, self.master, self.m, self.v, self.n,
+                                   self.d_table, len(self.table),
+                                   self.zs.hparams(t, **self.w.hparams()), group=self.group,
+                                   micro_batches=self.micro_batches, acc=self.acc)
+        self.step_t = t
+
     def set_buckets(self, bucket_params: int) -> list:
         """ZeRO-2 style buckets: split the chunk table into contiguous runs of
         about bucket_params shard elements (whole chunks).  Each bucket is then
@@ -287,6 +306,10 @@ def main() -> int:
     ap.add_argument("--max-chunk", type=int, default=None,
                     help="chunk-table cut length (default: the library's tuned value)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--group", type=int, default=0,
+                    help="two-level reduce: ranks per group (hybrid sharding); 0 = flat")
+    ap.add_argument("--micro-batches", type=int, default=1,
+                    help="gradient accumulation: micro-batches per optimizer step")
     ap.add_argument("--bucket-params", type=int, default=0,
                     help="step the shard in buckets of about this many params, one launch "
                          "per bucket (ZeRO-2 bucketed step); 0 = one launch per step")
@@ -313,9 +336,15 @@ def main() -> int:
           f"dst={sh.dst_mode}, first timed step t={t + args.warmup}", file=sys.stderr, flush=True)
 
     step = sh.step
+    extended = args.group > 0 or args.micro_batches > 1
+    if extended and args.bucket_params > 0:
+        raise SystemExit("--bucket-params does not combine with --group/--micro-batches")
     if args.bucket_params > 0:
         sh.set_buckets(args.bucket_params)
         step = sh.step_bucketed
+    elif extended:
+        sh.set_extended(args.group, args.micro_batches)
+        step = sh.step_extended
     for _ in range(args.warmup):
         step(t)
         t += 1
@@ -331,13 +360,34 @@ def main() -> int:
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    ms_per_step = wall * 1e3 / args.steps
     launches = len(sh.buckets) if args.bucket_params > 0 else 1
     kernel_ms = ev0.elapsed_time(ev1) / args.steps / launches   # average launch
-    ms_per_step = wall * 1e3 / args.steps
+    ext = None
+    if extended:
+        # Time the final fused launch on its own (same state, next steps) so
+        # the roofline is the fused kernel's; the step time above includes
+        # the accumulation passes.
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e2.record(stream)
+        for _ in range(args.steps):
+            sh.zs.zero_shard_step_ex(sh.partials, sh.master, sh.m, sh.v, sh.n, sh.d_table,
+                                     len(sh.table), sh.zs.hparams(t, **w.hparams()),
+                                     group=args.group, micro_batches=args.micro_batches,
+                                     acc=sh.acc)
+            t += 1
+        e3.record(stream)
+        torch.cuda.synchronize()
+        kernel_ms = e2.elapsed_time(e3) / args.steps
+        ext = {"group": args.group, "micro_batches": args.micro_batches,
+               "step_ms_including_accumulation": ms_per_step}
 
     bytes_launch = sh.bytes_per_launch() / launches
+    if extended and args.micro_batches > 1:
+        bytes_launch += 4 * sh.n           # the accumulator read by the fused launch
     achieved = bytes_launch / (kernel_ms * 1e-3) / 1e9
-    kernel_key = f"shard_step_kernel<{w.gdt},{w.n_ranks}>/{w.name}"
+    kernel_key = f"shard_step_kernel<{w.gdt},{w.n_ranks}{',ext' if extended else ''}>/{w.name}"
     traffic = load_traffic(kernel_key) if launches == 1 else None
     out = {
         "metric": "params updated/sec and achieved HBM GB/s (fraction of peak), fused shard step",
@@ -365,6 +415,8 @@ def main() -> int:
                      "kernel": kernel_key, "kernel_ms": kernel_ms,
                      "algorithmic_bytes_per_launch": bytes_launch},
     }
+    if ext is not None:
+        out["extended_reduce"] = ext
     if args.probe_copy > 0:
         out["probe_copy"] = probe_copy(args.probe_copy)
     if not args.no_cpu_baseline:

@@ -233,10 +233,13 @@ __device__ __forceinline__ void fold_finish(double *s, const double *t, int n, i
     }
 }
 
-template <zero_dtype G, int NC>
+// KC > 0: group size known at compile time, so after unrolling every group
+// boundary test folds away; KC == 0: K at run time (scalar branches).
+template <zero_dtype G, int NC, int KC>
 __device__ __forceinline__ void group_sum_two_level(double *s, const PartialPtrs &pp, int n_rt,
-                                                    int K, int64_t i0)
+                                                    int K_rt, int64_t i0)
 {
+    const int K = KC > 0 ? KC : K_rt;
     using GT = Grad<G>;
     constexpr int VEC = GT::VEC;
     const int64_t off = i0 * GT::BYTES;
@@ -328,7 +331,7 @@ __device__ __forceinline__ void store_bf16(uint16_t *dst, const uint32_t *h, boo
 
 // EXT: the extended reduce of zero_shard_step_ex (two-level order, optional
 // accumulator of earlier micro-batches, divisor N * micro-batches).
-template <zero_dtype G, int NC, bool EXT>
+template <zero_dtype G, int NC, bool EXT, int KC>
 __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &c)
 {
     constexpr int VEC = Grad<G>::VEC;
@@ -353,7 +356,10 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
                 F32x<VEC> acc;
                 if (a.acc)
                     acc.load(a.acc + i0);
-                group_sum_two_level<G, NC>(s, a.parts, n, a.red.group, i0);
+                if constexpr (KC < 0)
+                    group_sum<G, NC>(s, a.parts, n, i0);
+                else
+                    group_sum_two_level<G, NC, KC>(s, a.parts, n, a.red.group, i0);
                 if (a.acc) {
 #pragma unroll
                     for (int j = 0; j < VEC; ++j)
@@ -405,12 +411,14 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
 // read/write stream, measured across chunk sizes and block shapes on
 // MI355X (4 resident waves per CU beat 8-16).  Each wave still keeps its
 // group's 14 (N = 8) to 22 (N = 16) 16-byte loads in flight at once.
-template <zero_dtype G, int NC, bool EXT>
+// KC (extended step only): -1 flat rank order, 0 two-level with the group
+// size at run time, > 0 two-level with that group size.
+template <zero_dtype G, int NC, bool EXT, int KC = -1>
 __global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void shard_step_kernel(StepArgs a)
 {
     for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
-        step_chunk<G, NC, EXT>(a, chunk_at(a.chunks, ci));
+        step_chunk<G, NC, EXT, KC>(a, chunk_at(a.chunks, ci));
 }
 
 // ---------------------------------------------------------------- unfused
@@ -440,27 +448,39 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a)
 }
 
 // One non-final micro-batch: acc = fp32((reset ? 0 : acc) + two-level sum).
-template <zero_dtype G, int NC>
-__global__ __launch_bounds__(kBlock) void accumulate_kernel(AccArgs a)
+// Launched like the step kernel: one wave per workgroup, at most one wave
+// per SIMD; workgroup b walks spans b, b + gridDim.x, ... of kAccSpan
+// consecutive elements.
+constexpr int64_t kAccSpan = 2048;
+
+template <zero_dtype G, int NC, int KC>
+__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void accumulate_kernel(AccArgs a)
 {
     constexpr int VEC = Grad<G>::VEC;
+    constexpr int64_t GPS = kAccSpan / VEC;   // groups per span
     const int n = NC > 0 ? NC : a.red.n_ranks;
     const int64_t groups = a.n / VEC;
-    for (int64_t g = (int64_t)blockIdx.x * kBlock + threadIdx.x; g < groups;
-         g += (int64_t)gridDim.x * kBlock) {
-        const int64_t i0 = g * VEC;
-        F32x<VEC> acc;
-        if (!a.reset)
-            acc.load(a.acc + i0);
-        double s[VEC];
-        group_sum_two_level<G, NC>(s, a.parts, n, a.red.group, i0);
+    for (int64_t sp = blockIdx.x; sp * GPS < groups; sp += gridDim.x) {
+        const int64_t gend = (sp + 1) * GPS < groups ? (sp + 1) * GPS : groups;
+        for (int64_t g = sp * GPS + threadIdx.x; g < gend; g += kStepBlock) {
+            const int64_t i0 = g * VEC;
+            F32x<VEC> acc;
+            if (!a.reset)
+                acc.load(a.acc + i0);
+            double s[VEC];
+            if constexpr (KC < 0)
+                group_sum<G, NC>(s, a.parts, n, i0);
+            else
+                group_sum_two_level<G, NC, KC>(s, a.parts, n, a.red.group, i0);
 #pragma unroll
-        for (int j = 0; j < VEC; ++j)
-            acc[j] = a.reset ? (float)s[j] : (float)((double)acc[j] + s[j]);
-        acc.store(a.acc + i0);
+            for (int j = 0; j < VEC; ++j)
+                acc[j] = a.reset ? (float)s[j] : (float)((double)acc[j] + s[j]);
+            acc.store(a.acc + i0);
+        }
     }
     if (blockIdx.x == 0) {
-        const int64_t i = groups * VEC + threadIdx.x;
+        const int64_t i = groups * VEC + threadIdx.x;   // the last n % VEC elements
         if (i < a.n) {
             const double e = elem_sum_two_level<G>(a.parts, n, a.red.group, i);
             a.acc[i] = a.reset ? (float)e : (float)((double)a.acc[i] + e);
@@ -590,25 +610,83 @@ hipError_t launch_step(const StepArgs &a, zero_dtype gdt, hipStream_t s)
                             : step_dispatch<ZERO_FP32, false>(a, s);
 }
 
+// The extended step picks its fold at launch: groups of 1 or of all N ranks
+// are the flat order (KC = -1); groups of 4 or 8 (GPUs per node) have
+// compiled folds for N in {8, 16, 32, 64}; any other grouping runs the
+// run-time fold (KC = 0).
+template <zero_dtype G, int NC>
+static void launch_ex_n(const StepArgs &a, int K, dim3 grid, dim3 block, hipStream_t s)
+{
+    if (K == 1 || K == a.red.n_ranks)
+        hipLaunchKernelGGL((shard_step_kernel<G, NC, true, -1>), grid, block, 0, s, a);
+    else if (NC % 8 == 0 && NC > 8 && K == 8)
+        hipLaunchKernelGGL((shard_step_kernel<G, NC, true, (NC % 8 == 0 && NC > 8) ? 8 : 0>), grid, block, 0, s, a);
+    else if (NC % 4 == 0 && NC > 4 && K == 4)
+        hipLaunchKernelGGL((shard_step_kernel<G, NC, true, (NC % 4 == 0 && NC > 4) ? 4 : 0>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((shard_step_kernel<G, NC, true, 0>), grid, block, 0, s, a);
+}
+
+template <zero_dtype G>
+static hipError_t step_ex_dispatch(const StepArgs &a, hipStream_t s)
+{
+    dim3 grid(chunk_grid(a.n_chunks)), block(kStepBlock);
+    const int K = a.red.group;
+    switch (a.red.n_ranks) {
+    case 1: launch_ex_n<G, 1>(a, K, grid, block, s); break;
+    case 2: launch_ex_n<G, 2>(a, K, grid, block, s); break;
+    case 4: launch_ex_n<G, 4>(a, K, grid, block, s); break;
+    case 8: launch_ex_n<G, 8>(a, K, grid, block, s); break;
+    case 16: launch_ex_n<G, 16>(a, K, grid, block, s); break;
+    case 32: launch_ex_n<G, 32>(a, K, grid, block, s); break;
+    case 64: launch_ex_n<G, 64>(a, K, grid, block, s); break;
+    default:
+        if (K == 1 || K == a.red.n_ranks)
+            hipLaunchKernelGGL((shard_step_kernel<G, 0, true, -1>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((shard_step_kernel<G, 0, true, 0>), grid, block, 0, s, a);
+        break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_step_ex(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 {
-    return gdt == ZERO_BF16 ? step_dispatch<ZERO_BF16, true>(a, s)
-                            : step_dispatch<ZERO_FP32, true>(a, s);
+    return gdt == ZERO_BF16 ? step_ex_dispatch<ZERO_BF16>(a, s) : step_ex_dispatch<ZERO_FP32>(a, s);
+}
+
+template <zero_dtype G, int NC>
+static void launch_acc_n(const AccArgs &a, int K, dim3 grid, dim3 block, hipStream_t s)
+{
+    if (K == 1 || K == a.red.n_ranks)
+        hipLaunchKernelGGL((accumulate_kernel<G, NC, -1>), grid, block, 0, s, a);
+    else if (NC % 8 == 0 && NC > 8 && K == 8)
+        hipLaunchKernelGGL((accumulate_kernel<G, NC, (NC % 8 == 0 && NC > 8) ? 8 : 0>), grid, block, 0, s, a);
+    else if (NC % 4 == 0 && NC > 4 && K == 4)
+        hipLaunchKernelGGL((accumulate_kernel<G, NC, (NC % 4 == 0 && NC > 4) ? 4 : 0>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((accumulate_kernel<G, NC, 0>), grid, block, 0, s, a);
 }
 
 template <zero_dtype G>
 static hipError_t accumulate_dispatch(const AccArgs &a, hipStream_t s)
 {
-    dim3 grid(grid_for(a.n / Grad<G>::VEC + 1)), block(kBlock);
+    dim3 grid(chunk_grid((a.n + kAccSpan - 1) / kAccSpan)), block(kStepBlock);
+    const int K = a.red.group;
     switch (a.red.n_ranks) {
-    case 1: hipLaunchKernelGGL((accumulate_kernel<G, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((accumulate_kernel<G, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((accumulate_kernel<G, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((accumulate_kernel<G, 8>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((accumulate_kernel<G, 16>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((accumulate_kernel<G, 32>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((accumulate_kernel<G, 64>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((accumulate_kernel<G, 0>), grid, block, 0, s, a); break;
+    case 1: launch_acc_n<G, 1>(a, K, grid, block, s); break;
+    case 2: launch_acc_n<G, 2>(a, K, grid, block, s); break;
+    case 4: launch_acc_n<G, 4>(a, K, grid, block, s); break;
+    case 8: launch_acc_n<G, 8>(a, K, grid, block, s); break;
+    case 16: launch_acc_n<G, 16>(a, K, grid, block, s); break;
+    case 32: launch_acc_n<G, 32>(a, K, grid, block, s); break;
+    case 64: launch_acc_n<G, 64>(a, K, grid, block, s); break;
+    default:
+        if (K == 1 || K == a.red.n_ranks)
+            hipLaunchKernelGGL((accumulate_kernel<G, 0, -1>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((accumulate_kernel<G, 0, 0>), grid, block, 0, s, a);
+        break;
     }
     return hipGetLastError();
 }
