@@ -54,13 +54,19 @@ def _load(path: str):
     L.oracle_accumulate.argtypes = [vp, i32, i32, i32, i64, vp, i32]
     L.oracle_shard_step_ex.argtypes = [vp, i32, i32, i32, vp, i64, i64, vp, vp, vp,
                                        ctypes.POINTER(HParams), vp]
+    L.oracle_bf16_from_double.argtypes = [ctypes.c_double]
+    L.oracle_bf16_from_double.restype = ctypes.c_uint16
+    L.oracle_bf16_from_double_array.argtypes = [vp, i64, vp]
+    L.oracle_shard_step_bf16m.argtypes = [vp, i32, i32, i64, vp, vp, vp,
+                                          ctypes.POINTER(HParams), vp]
     L.oracle_shard_segments.argtypes = [vp, i32, i32, i32, vp, i64, ctypes.POINTER(i64)]
     L.oracle_shard_segments.restype = i64
     L.oracle_set_threads.argtypes = [i32]
     L.oracle_max_threads.restype = i32
     for f in (L.oracle_bf16_round_array, L.oracle_reduce, L.oracle_adamw,
               L.oracle_shard_step, L.oracle_set_threads, L.oracle_reduce_ex,
-              L.oracle_accumulate, L.oracle_shard_step_ex):
+              L.oracle_accumulate, L.oracle_shard_step_ex, L.oracle_bf16_from_double_array,
+              L.oracle_shard_step_bf16m):
         f.restype = None
     return L
 
@@ -186,6 +192,27 @@ def shard_step_ex(partials: Sequence[np.ndarray], master, m, v, hp: HParams, gro
     lib().oracle_shard_step_ex(_ptr_array(partials), len(partials), _group_of(len(partials), group),
                                _gdt(partials), None if a is None else _p(a), micro_batches, n,
                                _p(th), _p(mm), _p(vv), ctypes.byref(hp), _p(prm))
+    return th, mm, vv, prm
+
+
+def bf16_from_double(x: np.ndarray) -> np.ndarray:
+    """Nearest-even bf16 bits of float64 values, one rounding."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().oracle_bf16_from_double_array(_p(x), x.size, _p(out))
+    return out
+
+
+def shard_step_bf16m(partials: Sequence[np.ndarray], master, m_bits, v_bits, hp: HParams):
+    """Shard step on the 12-byte state (bf16 m, v as uint16 bits); returns
+    (master, m_bits, v_bits, param_bits)."""
+    n = master.size
+    th = np.array(master, dtype=np.float32, copy=True)
+    mm = np.array(m_bits, dtype=np.uint16, copy=True)
+    vv = np.array(v_bits, dtype=np.uint16, copy=True)
+    prm = np.empty(n, dtype=np.uint16)
+    lib().oracle_shard_step_bf16m(_ptr_array(partials), len(partials), _gdt(partials), n,
+                                  _p(th), _p(mm), _p(vv), ctypes.byref(hp), _p(prm))
     return th, mm, vv, prm
 
 

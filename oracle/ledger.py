@@ -47,14 +47,17 @@ class Ledger:
 # bf16 parameter + bf16 gradient + fp32 master, m, v.
 MIXED_PRECISION_ADAM = Ledger(param=2, grad=2, optimizer=4 + 4 + 4)
 
+# Everything but the fp32 master in bf16: 2 + 2 + (4 master + 2 m + 2 v).
+BF16_MOMENTS_ADAM = Ledger(param=2, grad=2, optimizer=4 + 2 + 2)
+
 # Element sizes of the arrays the shard step reads and writes: bf16 param
 # slot, bf16 gradient partial, fp32 master, fp32 m, fp32 v.
 STATE_ELEMENT_BYTES = {"param": 2, "grad": 2, "master": 4, "m": 4, "v": 4}
 
 
-def shard_step_bytes_per_param(n_ranks: int, grad_bytes: int = 2) -> int:
+def shard_step_bytes_per_param(n_ranks: int, grad_bytes: int = 2, moment_bytes: int = 4) -> int:
     """HBM bytes the fused step must move per shard element: read N gradient
-    partials and the fp32 master, m, v; write master, m, v and the 16-bit
-    parameter."""
+    partials and the master, m, v; write master, m, v and the 16-bit
+    parameter.  moment_bytes = 2 for the 12-byte ledger's bf16 moments."""
     s = STATE_ELEMENT_BYTES
-    return n_ranks * grad_bytes + 2 * (s["master"] + s["m"] + s["v"]) + s["param"]
+    return n_ranks * grad_bytes + 2 * (s["master"] + 2 * moment_bytes) + s["param"]

@@ -181,6 +181,56 @@ static float reduce_ex_one(const void *const *partials, int n_ranks, int group, 
     return (float)(s / ((double)n_ranks * (double)micro_batches));
 }
 
+/*
+ * The 12-bytes-per-parameter ledger ("并行训练优化、MoE扩展与系统瓶颈", 2.2.9:
+ * everything but the master weights in BF16 comes to about 12 bytes per
+ * parameter; the same 2 + 2 + 8 split sizes the capacity table of Lecture 8,
+ * Slide 28): bf16 parameter and gradient, fp32 master, bf16 Adam m and v.
+ * The update is the AdamW above with the moments read from and rounded back
+ * to bf16: m' and v' (double) are each rounded once, to nearest even, straight
+ * to bf16.
+ *
+ * Rounding a double to bf16 (8 significant bits, fp32's exponent range):
+ * write |d| = f 2^E with 1/2 <= f < 1; the candidates are the multiples of
+ * 2^(E-8), or of 2^-133 below the normal range (bf16 subnormals); rint()
+ * rounds the scaled value to the nearest integer, ties to even, exactly.
+ * Results above the largest finite bf16 (0x7F7F = (2^8 - 1) 2^120) become inf.
+ */
+uint16_t oracle_bf16_from_double(double d)
+{
+    if (isnan(d)) {
+        float f = (float)d;                       /* keeps the sign; quiet */
+        uint32_t u;
+        memcpy(&u, &f, 4);
+        return (uint16_t)((u >> 16) | 0x0040u);
+    }
+    double a = fabs(d);
+    double r = 0.0;
+    if (a != 0.0 && !isinf(a)) {
+        int E;
+        frexp(a, &E);                             /* a = f 2^E, 1/2 <= f < 1 */
+        int q = E - 8;                            /* spacing 2^q of 8-bit significands */
+        if (q < -133)
+            q = -133;                             /* subnormal spacing */
+        r = ldexp(rint(ldexp(a, -q)), q);         /* exact scaling, one rounding */
+        if (r > ldexp(255.0, 120))
+            r = INFINITY;
+    } else {
+        r = a;
+    }
+    float f = (float)(signbit(d) ? -r : r);       /* exact: r has <= 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+void oracle_bf16_from_double_array(const double *in, int64_t n, uint16_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_from_double(in[i]);
+}
+
 /* ---- array entry points --------------------------------------------- */
 
 /* g_out[i] = fp32( (p_0[i] + p_1[i] + ... + p_{N-1}[i]) / N ), i in [0, n). */
@@ -249,6 +299,30 @@ void oracle_shard_step_ex(const void *const *partials, int n_ranks, int group, i
     for (int64_t i = 0; i < n; ++i) {
         float g = reduce_ex_one(partials, n_ranks, group, gdt, acc, micro_batches, i);
         adamw_one(g, &master[i], &m[i], &v[i], hp, bc1, bc2);
+        if (param_out)
+            param_out[i] = oracle_bf16_round(master[i]);
+    }
+}
+
+/* The shard step on the 12-byte state: m, v are bf16 bit patterns. */
+void oracle_shard_step_bf16m(const void *const *partials, int n_ranks, int gdt, int64_t n,
+                             float *master, uint16_t *m, uint16_t *v, const oracle_hparams *hp,
+                             uint16_t *param_out)
+{
+    double bc1 = bias_correction(hp->beta1, hp->step);
+    double bc2 = bias_correction(hp->beta2, hp->step);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double g = reduce_one(partials, n_ranks, gdt, i);
+        double m1 = hp->beta1 * bf16_value(m[i]) + (1.0 - hp->beta1) * g;
+        double v1 = hp->beta2 * bf16_value(v[i]) + (1.0 - hp->beta2) * (g * g);
+        double mhat = m1 / bc1;
+        double vhat = v1 / bc2;
+        double upd = mhat / (sqrt(vhat) + hp->eps);
+        double th = (double)master[i] * (1.0 - hp->lr * hp->weight_decay) - hp->lr * upd;
+        m[i] = oracle_bf16_from_double(m1);
+        v[i] = oracle_bf16_from_double(v1);
+        master[i] = (float)th;
         if (param_out)
             param_out[i] = oracle_bf16_round(master[i]);
     }

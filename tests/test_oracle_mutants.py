@@ -15,6 +15,7 @@ import pytest
 import oracle
 import test_oracle_pins as pins
 import test_oracle_pins_ex as pins_ex
+import test_oracle_pins_bf16m as pins_m
 
 MUTANTS = {
     "drop_last_rank": ("for (int k = 1; k < n_ranks; ++k)", "for (int k = 1; k < n_ranks - 1; ++k)"),
@@ -48,6 +49,13 @@ MUTANTS = {
     "divisor_ignores_micro_batches": ("(double)n_ranks * (double)micro_batches", "(double)n_ranks"),
     "accumulate_reset_ignored": ("acc[i] = reset ? (float)s : (float)((double)acc[i] + s);",
                                  "acc[i] = (float)((double)acc[i] + s);"),
+    "bf16d_truncates": ("r = ldexp(rint(ldexp(a, -q)), q);", "r = ldexp(floor(ldexp(a, -q)), q);"),
+    "bf16d_spacing": ("int q = E - 8;", "int q = E - 9;"),
+    "bf16m_moment_through_fp32": ("m[i] = oracle_bf16_from_double(m1);",
+                                  "m[i] = oracle_bf16_round((float)m1);"),
+    "bf16m_v_from_m": ("v[i] = oracle_bf16_from_double(v1);", "v[i] = oracle_bf16_from_double(m1);"),
+    "bf16m_beta_swapped": ("hp->beta1 * bf16_value(m[i]) + (1.0 - hp->beta1) * g",
+                           "(1.0 - hp->beta1) * bf16_value(m[i]) + hp->beta1 * g"),
     "accumulate_rounds_twice": ("acc[i] = reset ? (float)s : (float)((double)acc[i] + s);",
                                 "acc[i] = reset ? (float)s : (float)((double)acc[i] + (double)(float)s);"),
 }
@@ -69,6 +77,11 @@ FAST_PINS = [
     lambda: pins_ex.test_grouped_mean_is_exact_when_sums_are_exact(8, 2),
     lambda: pins_ex.test_accumulated_micro_batches_give_the_full_batch_gradient(2),
     lambda: pins_ex.test_accumulator_rounds_once_per_micro_batch(),
+    lambda: pins_m.test_double_to_bf16_matches_brute_force(),
+    lambda: pins_m.test_double_to_bf16_is_one_rounding(),
+    lambda: pins_m.test_bf16_moment_step_equals_fp32_step_when_moments_are_exact(),
+    lambda: pins_m.test_bf16_moment_step_rounds_moments_to_nearest(),
+    lambda: pins_m.test_bf16_moment_step_rounds_once(),
 ]
 
 
