@@ -212,6 +212,21 @@ int zero_accumulate_shard(const void *const *partials, int n_ranks, zero_dtype g
                           int64_t n, float *acc, int reset, hipStream_t stream);
 
 /*
+ * The fused step on the 12-bytes-per-parameter state ("并行训练优化、MoE扩展与
+ * 系统瓶颈", 2.2.9: everything but the master weights in BF16 comes to about
+ * 12 bytes per parameter): fp32 master, bf16 Adam moments m and v (16-bit
+ * patterns, shard_len each, updated in place).  Reduce and AdamW as
+ * zero_shard_step, with the moments widened exactly from bf16 and the new
+ * m', v' rounded once, from double, to nearest-even bf16.  Moves 2N + 18
+ * bytes per element (bf16 partials) instead of 2N + 26.  Errors as
+ * zero_shard_step.
+ */
+int zero_shard_step_bf16_moments(const void *const *partials, int n_ranks, zero_dtype gdt,
+                                 float *master, uint16_t *m, uint16_t *v, int64_t shard_len,
+                                 const zero_chunk *d_chunks, int64_t n_chunks,
+                                 const zero_adamw_hparams *hp, hipStream_t stream);
+
+/*
  * Reduce only: grad_out[i] = fp32((p_0[i] + ... + p_{N-1}[i]) / N),
  * i in [0, n), summed in double in rank order.  grad_out must not overlap
  * any partial (ALIAS).  n == 0 is a no-op.

@@ -72,6 +72,8 @@ _lib.zero_shard_step.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64
 _lib.zero_shard_step_ex.argtypes = [_vp, _i32, _i32, ctypes.POINTER(ReduceSpec), _vp, _vp, _vp,
                                     _i64, _vp, _i64, ctypes.POINTER(HParams), _vp]
 _lib.zero_accumulate_shard.argtypes = [_vp, _i32, _i32, _i32, _i64, _vp, _i32, _vp]
+_lib.zero_shard_step_bf16_moments.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64,
+                                              ctypes.POINTER(HParams), _vp]
 _lib.zero_reduce_shard.argtypes = [_vp, _i32, _i32, _i64, _vp, _vp]
 _lib.zero_adamw_shard.argtypes = [_vp, _vp, _vp, _vp, _i64, ctypes.POINTER(HParams), _vp]
 _lib.zero_gather_write.argtypes = [_vp, _i64, _vp, _i64, _vp]
@@ -80,7 +82,7 @@ _lib.zero_strerror.argtypes = [_i32]
 _lib.zero_strerror.restype = ctypes.c_char_p
 for _f in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
            "zero_gather_write", "zero_probe_copy", "zero_version", "zero_shard_step_ex",
-           "zero_accumulate_shard"):
+           "zero_accumulate_shard", "zero_shard_step_bf16_moments"):
     getattr(_lib, _f).restype = _i32
 
 Ptr = Union[int, "torch.Tensor", None]  # noqa: F821
@@ -193,6 +195,18 @@ def zero_shard_step_ex(partials: Sequence[Ptr], master: Ptr, m: Ptr, v: Ptr, sha
                                    _addr(master), _addr(m), _addr(v), shard_len, _addr(d_chunks),
                                    n_chunks, ctypes.byref(hp), _stream(stream)),
            "zero_shard_step_ex")
+
+
+def zero_shard_step_bf16_moments(partials: Sequence[Ptr], master: Ptr, m: Ptr, v: Ptr,
+                                 shard_len: int, d_chunks: Ptr, n_chunks: int, hp: HParams,
+                                 gdt: Optional[int] = None, stream=None) -> None:
+    """Fused step on the 12-byte state: fp32 master, bf16 m and v (int16 /
+    bfloat16 tensors holding the bit patterns)."""
+    gdt = _gdt_of(partials) if gdt is None else gdt
+    _check(_lib.zero_shard_step_bf16_moments(_partial_array(partials), len(partials), gdt,
+                                             _addr(master), _addr(m), _addr(v), shard_len,
+                                             _addr(d_chunks), n_chunks, ctypes.byref(hp),
+                                             _stream(stream)), "zero_shard_step_bf16_moments")
 
 
 def zero_accumulate_shard(partials: Sequence[Ptr], n: int, acc: Ptr, reset: bool,

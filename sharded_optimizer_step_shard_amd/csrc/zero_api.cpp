@@ -124,7 +124,7 @@ bool in_device_alloc(const void *p, int64_t bytes)
 
 extern "C" {
 
-int zero_version(void) { return (1 << 16) | 1; }
+int zero_version(void) { return (1 << 16) | 2; }
 
 const char *zero_strerror(int code)
 {
@@ -301,6 +301,47 @@ int zero_shard_step_ex(const void *const *partials, int n_ranks, zero_dtype gdt,
     a.shard_len = shard_len;
     a.acc = rs->acc;
     return hip_status(launch_step_ex(a, gdt, stream));
+}
+
+int zero_shard_step_bf16_moments(const void *const *partials, int n_ranks, zero_dtype gdt,
+                                 float *master, uint16_t *m, uint16_t *v, int64_t shard_len,
+                                 const zero_chunk *d_chunks, int64_t n_chunks,
+                                 const zero_adamw_hparams *hp, hipStream_t stream)
+{
+    StepArgs a;
+    int rc = check_partials(partials, n_ranks, gdt, shard_len, a.parts);
+    if (rc)
+        return rc;
+    if (((!master || !m || !v) && shard_len > 0) || shard_len < 0 || n_chunks < 0 ||
+        n_chunks > INT32_MAX || (n_chunks > 0 && !d_chunks) || !valid_hparams(hp))
+        return ZERO_ERR_INVALID;
+    if (!aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(d_chunks))
+        return ZERO_ERR_MISALIGNED;
+    const int64_t fb = shard_len * 4, hb = shard_len * 2, gb = shard_len * elem_bytes(gdt);
+    if (overlaps(master, fb, m, hb) || overlaps(master, fb, v, hb) || overlaps(m, hb, v, hb))
+        return ZERO_ERR_ALIAS;
+    for (int k = 0; k < n_ranks; ++k)
+        if (overlaps(partials[k], gb, master, fb) || overlaps(partials[k], gb, m, hb) ||
+            overlaps(partials[k], gb, v, hb))
+            return ZERO_ERR_ALIAS;
+    if (n_chunks == 0 || shard_len == 0)
+        return ZERO_OK;
+    for (int k = 0; k < n_ranks; ++k)
+        if (!in_device_alloc(partials[k], gb))
+            return ZERO_ERR_NOT_DEVICE;
+    if (!in_device_alloc(master, fb) || !in_device_alloc(m, hb) || !in_device_alloc(v, hb) ||
+        !in_device_alloc(d_chunks, n_chunks * (int64_t)sizeof(zero_chunk)))
+        return ZERO_ERR_NOT_DEVICE;
+    a.red = make_reduce(n_ranks);
+    a.k = make_scalars(hp);
+    a.master = master;
+    a.m = (float *)m;        // the kernel reads these as 16-bit patterns
+    a.v = (float *)v;
+    a.chunks = d_chunks;
+    a.n_chunks = n_chunks;
+    a.shard_len = shard_len;
+    a.acc = nullptr;
+    return hip_status(launch_step_m16(a, gdt, stream));
 }
 
 int zero_accumulate_shard(const void *const *partials, int n_ranks, zero_dtype gdt, int group,

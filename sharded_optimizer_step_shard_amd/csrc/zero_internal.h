@@ -77,6 +77,7 @@ struct GatherArgs {
 
 hipError_t launch_step(const StepArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_step_ex(const StepArgs &a, zero_dtype gdt, hipStream_t s);
+hipError_t launch_step_m16(const StepArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_accumulate(const AccArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs &a, hipStream_t s);

@@ -66,19 +66,48 @@ __device__ __forceinline__ float finish_reduce(double s, const ReduceScalars &r)
         return (float)(r.pow2 ? s * r.inv_n : s / r.n);
 }
 
-__device__ __forceinline__ void adamw(float g32, float &th, float &m, float &v, const StepScalars &k)
+// AdamW on one element: moments in and out in double (the caller stores
+// them in their format), master in and out in fp32.
+__device__ __forceinline__ void adamw_d(float g32, float &th, double m0, double v0, double &m1,
+                                        double &v1, const StepScalars &k)
 {
     double g = (double)g32;
-    double m1 = k.b1 * (double)m + k.c1 * g;
-    double v1 = k.b2 * (double)v + k.c2 * (g * g);
+    m1 = k.b1 * m0 + k.c1 * g;
+    v1 = k.b2 * v0 + k.c2 * (g * g);
     double mhat = m1 / k.bc1;
     double vhat = v1 / k.bc2;
     double upd = mhat / (__builtin_sqrt(vhat) + k.eps);
     double t1 = (double)th * k.dec - k.lr * upd;
-    m = (float)m1;
-    v = (float)v1;
     th = (float)t1;
 }
+
+__device__ __forceinline__ void adamw(float g32, float &th, float &m, float &v, const StepScalars &k)
+{
+    double m1, v1;
+    adamw_d(g32, th, (double)m, (double)v, m1, v1, k);
+    m = (float)m1;
+    v = (float)v1;
+}
+
+// double -> bf16 with a single nearest-even rounding: first round to fp32
+// by round-to-odd (truncate toward zero, then set the last bit if anything
+// was dropped), then round that to bf16 to nearest even.  fp32 keeps 16
+// more bits than bf16 at every magnitude, subnormals included, so the odd
+// bit stands in for everything below it and the second rounding is the
+// correct one (Boldo & Melquiond, round-to-odd).
+__device__ __forceinline__ uint32_t bf16_from_double(double d)
+{
+    const float f = (float)d;
+    const double fd = (double)f;
+    uint32_t u = __float_as_uint(f);
+    if (__builtin_fabs(fd) > __builtin_fabs(d))
+        u -= 1;                       // rounded away from zero: one step back
+    if (fd != d)
+        u |= 1;                       // inexact: make it odd
+    return to_bf16(__uint_as_float(u));
+}
+
+__device__ __forceinline__ double bf16_to_double(uint32_t h) { return (double)__uint_as_float(h << 16); }
 
 template <typename T>
 __device__ __forceinline__ T ld(const T *p) { return *p; }
@@ -307,6 +336,33 @@ template <int VEC> struct F32x {
     __device__ __forceinline__ float &operator[](int j) { return e[j]; }
 };
 
+// VEC bf16 values at an aligned address (16 bytes for VEC = 8, 8 for 4):
+// the moments of the 12-byte state.
+template <int VEC> struct B16x {
+    uint32_t e[VEC];
+    __device__ __forceinline__ void load(const uint16_t *p)
+    {
+        if constexpr (VEC == 8) {
+            u32x4 w = ld((const u32x4 *)p);
+            e[0] = w.x & 0xFFFFu; e[1] = w.x >> 16; e[2] = w.y & 0xFFFFu; e[3] = w.y >> 16;
+            e[4] = w.z & 0xFFFFu; e[5] = w.z >> 16; e[6] = w.w & 0xFFFFu; e[7] = w.w >> 16;
+        } else {
+            u32x2 w = ld((const u32x2 *)p);
+            e[0] = w.x & 0xFFFFu; e[1] = w.x >> 16; e[2] = w.y & 0xFFFFu; e[3] = w.y >> 16;
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t *p) const
+    {
+        if constexpr (VEC == 8) {
+            u32x4 w = {e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+            st_nt((u32x4 *)p, w);
+        } else {
+            u32x2 w = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+            st_nt((u32x2 *)p, w);
+        }
+    }
+};
+
 // VEC bf16 values: one 16-byte (VEC = 8) or 8-byte (VEC = 4) store when the
 // destination is aligned for it, else element by element.
 template <int VEC>
@@ -411,6 +467,71 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
 // read/write stream, measured across chunk sizes and block shapes on
 // MI355X (4 resident waves per CU beat 8-16).  Each wave still keeps its
 // group's 14 (N = 8) to 22 (N = 16) 16-byte loads in flight at once.
+// The step on the 12-byte state: fp32 master, bf16 m and v (in a.m, a.v
+// as 16-bit patterns).  Same reduce and AdamW; the moments are read from
+// bf16 and rounded back to bf16 once, from double.
+template <zero_dtype G, int NC>
+__device__ __forceinline__ void step_chunk_m16(const StepArgs &a, const zero_chunk &c)
+{
+    constexpr int VEC = Grad<G>::VEC;
+    if (c.len <= 0 || c.shard_off < 0 || c.shard_off > a.shard_len - c.len)
+        return;
+    const int n = NC > 0 ? NC : a.red.n_ranks;
+    uint16_t *const m16 = (uint16_t *)a.m, *const v16 = (uint16_t *)a.v;
+    const int64_t lo = c.shard_off, hi = c.shard_off + c.len;
+    const int64_t g0 = lo / VEC, g1 = (hi + VEC - 1) / VEC;
+    const bool vec_ok = (((uintptr_t)c.dst - (uintptr_t)(2 * (lo - g0 * VEC))) % (2 * VEC)) == 0;
+    for (int64_t g = g0 + threadIdx.x; g < g1; g += kStepBlock) {
+        const int64_t i0 = g * VEC;
+        uint16_t *d = c.dst + (i0 - lo);
+        if (i0 >= lo && i0 + VEC <= hi) {
+            double s[VEC];
+            F32x<VEC> th;
+            B16x<VEC> m, v;
+            th.load(a.master + i0);
+            m.load(m16 + i0);
+            v.load(v16 + i0);
+            group_sum<G, NC>(s, a.parts, n, i0);
+            uint32_t h[VEC];
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                double m1, v1;
+                adamw_d(finish_reduce<NC>(s[j], a.red), th[j], bf16_to_double(m.e[j]),
+                        bf16_to_double(v.e[j]), m1, v1, a.k);
+                m.e[j] = bf16_from_double(m1);
+                v.e[j] = bf16_from_double(v1);
+                h[j] = to_bf16(th[j]);
+            }
+            th.store(a.master + i0);
+            m.store(m16 + i0);
+            v.store(v16 + i0);
+            store_bf16<VEC>(d, h, vec_ok);
+        } else {
+            for (int j = 0; j < VEC; ++j) {
+                const int64_t i = i0 + j;
+                if (i < lo || i >= hi)
+                    continue;
+                float th = a.master[i];
+                double m1, v1;
+                adamw_d(finish_reduce<NC>(elem_sum<G>(a.parts, n, i), a.red), th,
+                        bf16_to_double(m16[i]), bf16_to_double(v16[i]), m1, v1, a.k);
+                a.master[i] = th;
+                m16[i] = (uint16_t)bf16_from_double(m1);
+                v16[i] = (uint16_t)bf16_from_double(v1);
+                d[j] = (uint16_t)to_bf16(th);
+            }
+        }
+    }
+}
+
+template <zero_dtype G, int NC>
+__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void shard_step_m16_kernel(StepArgs a)
+{
+    for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
+        step_chunk_m16<G, NC>(a, chunk_at(a.chunks, ci));
+}
+
 // KC (extended step only): -1 flat rank order, 0 two-level with the group
 // size at run time, > 0 two-level with that group size.
 template <zero_dtype G, int NC, bool EXT, int KC = -1>
@@ -648,6 +769,28 @@ static hipError_t step_ex_dispatch(const StepArgs &a, hipStream_t s)
         break;
     }
     return hipGetLastError();
+}
+
+template <zero_dtype G>
+static hipError_t step_m16_dispatch(const StepArgs &a, hipStream_t s)
+{
+    dim3 grid(chunk_grid(a.n_chunks)), block(kStepBlock);
+    switch (a.red.n_ranks) {
+    case 1: hipLaunchKernelGGL((shard_step_m16_kernel<G, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((shard_step_m16_kernel<G, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((shard_step_m16_kernel<G, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((shard_step_m16_kernel<G, 8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((shard_step_m16_kernel<G, 16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((shard_step_m16_kernel<G, 32>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((shard_step_m16_kernel<G, 64>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((shard_step_m16_kernel<G, 0>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_step_m16(const StepArgs &a, zero_dtype gdt, hipStream_t s)
+{
+    return gdt == ZERO_BF16 ? step_m16_dispatch<ZERO_BF16>(a, s) : step_m16_dispatch<ZERO_FP32>(a, s);
 }
 
 hipError_t launch_step_ex(const StepArgs &a, zero_dtype gdt, hipStream_t s)

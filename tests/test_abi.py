@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(zs):
 
 
 def test_version_and_strerror(zs):
-    assert zs.zero_version() == (1, 1)
+    assert zs.zero_version() == (1, 2)
     for code in range(8):
         assert zs.zero_strerror(code) and zs.zero_strerror(code) != "unknown error code"
     assert zs.zero_strerror(99) == "unknown error code"

@@ -316,3 +316,72 @@ def test_grouping_decides_the_rounding_on_gpu(zs):
     assert np.all(host(acc) == 0.0)
     zs.zero_accumulate_shard(parts, 16, acc, reset=True, group=0)
     assert np.all(host(acc) == 1.0)
+
+
+# ------------------------------------------------------------ 12-byte state
+
+def _m16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).cuda()
+
+
+@pytest.mark.parametrize("n_ranks,gdt,total,rank", [(1, "bf16", 9_999, 0), (3, "bf16", 30_001, 2),
+                                                    (8, "bf16", 80_003, 7), (16, "bf16", 64_000, 5),
+                                                    (32, "f32", 50_021, 31), (5, "f32", 12_345, 1)])
+def test_bf16_moment_state_matches_oracle(zs, n_ranks, gdt, total, rank):
+    say(f"case: 12-byte state N={n_ranks} {gdt} total={total} rank={rank}")
+    w = W.Workload("m16", 93, [total], n_ranks, gdt, 1e-3)
+    lo, hi = w.shard_range(rank)
+    n = hi - lo
+    idx = np.arange(lo, hi, dtype=np.int64)
+    rng = np.random.default_rng(n_ranks)
+    th_h = host_master(w, idx)
+    m_h = oracle.bf16_from_double(rng.standard_normal(n) * 1e-4)
+    v_h = oracle.bf16_from_double(rng.random(n) * 1e-8)
+    full = torch.full((total,), -1, dtype=torch.int16, device="cuda")
+    master, m, v = dev(th_h), _m16_dev(m_h), _m16_dev(v_h)
+    table, _ = zs.zero_build_chunks([total], n_ranks, rank, slot_dst=full.data_ptr() + 2 * lo,
+                                    max_chunk=576)
+    d_table = zs.chunks_to_device(table)
+    for t in (3, 4, 5):
+        parts_h = host_partials(w, t, idx)
+        parts = [dev_bf16(p) if gdt == "bf16" else dev(p) for p in parts_h]
+        zs.zero_shard_step_bf16_moments(parts, master, m, v, n, d_table, len(table), zs.hparams(t, **HP))
+        th_h, m_h, v_h, p_h = oracle.shard_step_bf16m(parts_h, th_h, m_h, v_h, oracle.hparams(t, **HP))
+    fb = host(full)
+    assert_bitwise(host(master), th_h, "12-byte master")
+    assert_bitwise(host(m), m_h, "12-byte m")
+    assert_bitwise(host(v), v_h, "12-byte v")
+    assert_bitwise(fb[lo:hi], p_h, "12-byte param")
+    assert np.all(fb[:lo] == 0xFFFF) and np.all(fb[hi:] == 0xFFFF)
+
+
+def test_bf16_moment_rounding_at_midpoints(zs):
+    """Moments driven onto, and one fp32 ulp either side of, bf16 midpoints:
+    beta1 = beta2 = 1/2 and one fp32 partial g make m' = (m + g)/2 exactly;
+    g is chosen so that m' lands at t, t +- 2^-24 t, t +- 2^-40 t for bf16
+    midpoints t.  Every stored moment must be the single nearest-even
+    rounding the oracle computes."""
+    say("case: 12-byte state rounding at bf16 midpoints")
+    rng = np.random.default_rng(31)
+    k = 20000
+    base = rng.integers(0x3000, 0x4000, k).astype(np.uint32)
+    lo_b = (base << 16).view(np.float32).astype(np.float64)
+    hi_b = ((base + 1) << 16).view(np.float32).astype(np.float64)
+    t = (lo_b + hi_b) / 2
+    rel = np.array([0.0, 2.0 ** -24, -2.0 ** -24, 2.0 ** -40, -2.0 ** -40])[rng.integers(0, 5, k)]
+    target = t * (1 + rel)
+    m_bits = oracle.bf16_from_double(rng.standard_normal(k) * t)
+    m_val = (m_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    g = (2 * target - m_val).astype(np.float32)           # fp32 partial (one rank)
+    hp = dict(lr=1e-3, beta1=0.5, beta2=0.5, eps=1e-8, weight_decay=0.0)
+    th = (rng.standard_normal(k) * 0.02).astype(np.float32)
+    v_bits = m_bits.copy()
+    full = torch.empty(k, dtype=torch.int16, device="cuda")
+    table, _ = zs.zero_build_chunks([k], 1, 0, slot_dst=full)
+    master, m, v = dev(th), _m16_dev(m_bits), _m16_dev(v_bits)
+    zs.zero_shard_step_bf16_moments([dev(g)], master, m, v, k, zs.chunks_to_device(table), len(table),
+                                    zs.hparams(1, **hp))
+    want = oracle.shard_step_bf16m([g], th, m_bits, v_bits, oracle.hparams(1, **hp))
+    assert_bitwise(host(m), want[1], "moments at midpoints: m")
+    assert_bitwise(host(v), want[2], "moments at midpoints: v")
+    assert_bitwise(host(master), want[0], "moments at midpoints: master")
