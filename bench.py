@@ -154,6 +154,21 @@ class Shard:
                                 self.zs.hparams(t, **self.w.hparams()))
         self.step_t = t
 
+    def use_bf16_moments(self) -> None:
+        """Switch to the 12-byte state: bf16 m and v beside the fp32 master.
+        Set-up only: the current fp32 moments (zero, or warm-started) are
+        rounded to bf16 with torch; the step then keeps them in bf16."""
+        import torch
+        self.m = self.m.to(torch.bfloat16).view(torch.int16).contiguous()
+        self.v = self.v.to(torch.bfloat16).view(torch.int16).contiguous()
+        self.state = "bf16-moments"
+
+    def step_bf16_moments(self, t: int) -> None:
+        self.zs.zero_shard_step_bf16_moments(self.partials, self.master, self.m, self.v, self.n,
+                                             self.d_table, len(self.table),
+                                             self.zs.hparams(t, **self.w.hparams()))
+        self.step_t = t
+
     def set_extended(self, group: int, micro_batches: int) -> None:
         """Use the extended reduce: two-level order with `group` ranks per
         group, and gradient accumulation over `micro_batches` (the same
@@ -208,7 +223,8 @@ class Shard:
         return out
 
     def bytes_per_launch(self) -> int:
-        return self.w.bytes_per_param() * self.n
+        moments = 8 if getattr(self, "state", "fp32") == "fp32" else 4
+        return (self.w.bytes_per_param() - 2 * (8 - moments)) * self.n
 
 
 def bucket_runs(chunk_lens, bucket_params: int) -> list:
@@ -306,6 +322,9 @@ def main() -> int:
     ap.add_argument("--max-chunk", type=int, default=None,
                     help="chunk-table cut length (default: the library's tuned value)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--state", default="fp32", choices=["fp32", "bf16-moments"],
+                    help="optimizer state: fp32 master, m, v (16 B/param ledger) or fp32 "
+                         "master with bf16 m, v (12 B/param ledger)")
     ap.add_argument("--group", type=int, default=0,
                     help="two-level reduce: ranks per group (hybrid sharding); 0 = flat")
     ap.add_argument("--micro-batches", type=int, default=1,
@@ -339,6 +358,11 @@ def main() -> int:
     extended = args.group > 0 or args.micro_batches > 1
     if extended and args.bucket_params > 0:
         raise SystemExit("--bucket-params does not combine with --group/--micro-batches")
+    if args.state == "bf16-moments":
+        if extended or args.bucket_params > 0:
+            raise SystemExit("--state bf16-moments runs the plain fused step only")
+        sh.use_bf16_moments()
+        step = sh.step_bf16_moments
     if args.bucket_params > 0:
         sh.set_buckets(args.bucket_params)
         step = sh.step_bucketed
@@ -387,7 +411,8 @@ def main() -> int:
     if extended and args.micro_batches > 1:
         bytes_launch += 4 * sh.n           # the accumulator read by the fused launch
     achieved = bytes_launch / (kernel_ms * 1e-3) / 1e9
-    kernel_key = f"shard_step_kernel<{w.gdt},{w.n_ranks}{',ext' if extended else ''}>/{w.name}"
+    kname = "shard_step_m16_kernel" if args.state == "bf16-moments" else "shard_step_kernel"
+    kernel_key = f"{kname}<{w.gdt},{w.n_ranks}{',ext' if extended else ''}>/{w.name}"
     traffic = load_traffic(kernel_key) if launches == 1 else None
     out = {
         "metric": "params updated/sec and achieved HBM GB/s (fraction of peak), fused shard step",
@@ -403,9 +428,11 @@ def main() -> int:
         "dtype": "f64",
         "data": "synthetic",
         "config": {"workload": f"{w.name} rank-{args.rank} shard", "shard_params": sh.n,
-                   "n_ranks": w.n_ranks, "grad_dtype": w.gdt, "state_dtype": "fp32",
+                   "n_ranks": w.n_ranks, "grad_dtype": w.gdt,
+                   "state_dtype": "fp32" if args.state == "fp32" else "fp32 master, bf16 m/v",
                    "param_dtype": "bf16", "tensors": len(w.numels), "chunks": len(sh.table),
-                   "dst": sh.dst_mode, "bytes_per_param": w.bytes_per_param(),
+                   "dst": sh.dst_mode, "bytes_per_param": sh.bytes_per_launch() // sh.n,
+                   "state": args.state,
                    "launches_per_step": launches,
                    "parallelism": "one data-parallel rank's ZeRO shard"},
         "hbm_gbs": achieved,
