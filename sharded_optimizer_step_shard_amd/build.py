@@ -48,6 +48,22 @@ def build(verbose: bool = True, out: str = LIB, extra=()) -> str:
     return out
 
 
+def build_c_example(verbose: bool = True) -> str:
+    """The plain C consumer of the ABI used by the tests (gcc, no hipcc, no
+    Python): tests/c_abi/step_c."""
+    src = os.path.join(ROOT, "tests", "c_abi", "step_c.c")
+    out = os.path.join(ROOT, "tests", "c_abi", "step_c")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include",
+           "-I", INCLUDE, "-o", out, src, "-L", PKG, "-lzero_shard", f"-L{rocm}/lib", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../sharded_optimizer_step_shard_amd", f"-Wl,-rpath,{rocm}/lib"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_c_example(verbose=True)
     sys.exit(0)
