@@ -176,9 +176,13 @@ template <> struct Grad<ZERO_FP32> {
     }
 };
 
+// Gradient partials are read exactly once: non-temporal loads stream them
+// past the caches, which stay with the master, m and v lines that are read
+// and then rewritten in place.  (Measured on MI355X: +2-4% on the 7B and
+// 70B shards; non-temporal loads of the state as well cost ~15%.)
 __device__ __forceinline__ u32x4 ld_raw(const void *base, int64_t byte_off)
 {
-    return ld((const u32x4 *)((const char *)base + byte_off));
+    return __builtin_nontemporal_load((const u32x4 *)((const char *)base + byte_off));
 }
 
 // Sum of the N partials over one full group starting at element i0, in
