@@ -268,10 +268,31 @@ def cpu_baseline(w: W.Workload, rank: int, t: int, target_s: float = 10.0,
         elapsed += time.perf_counter() - t0
         done += n
         reps += 1
-    return {"value": done / elapsed, "unit": "params/s", "cores": oracle.max_threads(),
+    # the same oracle on one thread, on a quarter of the sample
+    cores = oracle.max_threads()
+    n1 = max(1, n // 4)
+    oracle.set_threads(1)
+    try:
+        sub = [p[:n1] for p in parts]
+        done1, elapsed1, reps1 = 0, 0.0, 0
+        while elapsed1 < target_s / 4:
+            t0 = time.perf_counter()
+            oracle.shard_step(sub, master[:n1].copy(), m[:n1].copy(), v[:n1].copy(),
+                              oracle.hparams(t + reps1, **w.hparams()), in_place=True)
+            elapsed1 += time.perf_counter() - t0
+            done1 += n1
+            reps1 += 1
+    finally:
+        oracle.set_threads(cores)
+    value = done / elapsed
+    return {"value": value, "unit": "params/s", "cores": cores,
             "kind": "oracle",
             "sample": f"first {n} elements of rank {rank}'s shard of {w.name}, N={w.n_ranks} "
-                      f"{w.gdt} partials, {reps} oracle steps in {elapsed:.1f} s"}
+                      f"{w.gdt} partials, {reps} oracle steps in {elapsed:.1f} s",
+            "host_gbs": value * w.bytes_per_param() / 1e9,
+            "single_thread": {"value": done1 / elapsed1, "unit": "params/s",
+                              "sample": f"first {n1} elements, {reps1} steps in {elapsed1:.1f} s"},
+            "cpu_model": cpu_model()}
 
 
 def probe_copy(nbytes: int, reps: int = 5) -> dict:
@@ -299,6 +320,41 @@ def probe_copy(nbytes: int, reps: int = 5) -> dict:
             "frac_of_peak": 2 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def probe_read(nbytes: int, reps: int = 5) -> dict:
+    """Read-only stream over nbytes with zero_probe_read: the attainable read
+    rate beside the copy rate (the step is 2:1 read/write)."""
+    import torch
+    import sharded_optimizer_step_shard_amd as zs
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    src.fill_(1)
+    zs.zero_probe_read(src, nbytes, sink)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        zs.zero_probe_read(src, nbytes, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, sink
+    torch.cuda.empty_cache()
+    return {"bytes_read": nbytes, "ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def load_traffic(kernel_key: str) -> dict:
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
@@ -309,6 +365,102 @@ def load_traffic(kernel_key: str) -> dict:
     if not rec or rec.get("source_hash") != kernel_source_hash():
         return None
     return rec
+
+
+def _csv_rows(path: str):
+    import csv
+    with open(path, newline="") as f:
+        yield from csv.DictReader(f)
+
+
+def _counter_per_dispatch(path: str, counter: str, name_part: str) -> tuple:
+    """Mean of one rocprofv3 counter (KiB per dispatch) over the dispatches of
+    the kernel whose name holds name_part, at its largest grid; returns
+    (mean, dispatch count, grid)."""
+    by_grid = {}
+    for r in _csv_rows(path):
+        if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+            by_grid.setdefault(int(r["Grid_Size"]), []).append(float(r["Counter_Value"]))
+    if not by_grid:
+        raise SystemExit(f"{path}: no {counter} rows for a kernel named *{name_part}*")
+    grid = max(by_grid)
+    vals = by_grid[grid]
+    return sum(vals) / len(vals), len(vals), grid
+
+
+def ingest_counters(fetch_csv: str, write_csv: str, w: "W.Workload", rank: int, state: str,
+                    probe_bytes: int) -> dict:
+    """HBM traffic of one full-shard step launch from two rocprofv3 counter
+    passes (FETCH_SIZE, then WRITE_SIZE) over the same bench command with
+    --probe-copy: the copy kernel's known bytes turn each counter's KiB into
+    bytes.  Records the result in profiles/traffic.json under the kernel
+    source's hash (bench reports it as roofline.traffic only while the
+    source is unchanged) and returns the record."""
+    kname = "shard_step_m16_kernel" if state == "bf16-moments" else "shard_step_kernel"
+    kernel_key = f"{kname}<{w.gdt},{w.n_ranks}>/{w.name}"
+    f_kb, f_n, grid = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", kname)
+    w_kb, w_n, _ = _counter_per_dispatch(write_csv, "WRITE_SIZE", kname)
+    pf_kb, _, _ = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", "probe_copy_kernel")
+    pw_kb, _, _ = _counter_per_dispatch(write_csv, "WRITE_SIZE", "probe_copy_kernel")
+    f_factor, w_factor = probe_bytes / pf_kb, probe_bytes / pw_kb
+    lo, hi = w.shard_range(rank)
+    n = hi - lo
+    mb = 4 if state == "fp32" else 2
+    alg_read = (w.n_ranks * (2 if w.gdt == "bf16" else 4) + 4 + 2 * mb) * n
+    alg_write = (4 + 2 * mb + 2) * n
+    rec = {
+        "source_hash": kernel_source_hash(),
+        "bytes_per_launch": f_kb * f_factor + w_kb * w_factor,
+        "fetch_bytes_per_launch": f_kb * f_factor,
+        "write_bytes_per_launch": w_kb * w_factor,
+        "algorithmic_read_bytes": alg_read,
+        "algorithmic_write_bytes": alg_write,
+        "fetch_over_algorithmic": f_kb * f_factor / alg_read,
+        "write_over_algorithmic": w_kb * w_factor / alg_write,
+        "total_over_algorithmic": (f_kb * f_factor + w_kb * w_factor) / (alg_read + alg_write),
+        "fetch_size_counter_kb_per_launch": f_kb,
+        "write_size_counter_kb_per_launch": w_kb,
+        "dispatches": [f_n, w_n],
+        "grid": grid,
+        "calibration": {
+            "kernel": "zs::probe_copy_kernel",
+            "bytes_read": probe_bytes,
+            "bytes_written": probe_bytes,
+            "fetch_size_kb": pf_kb,
+            "write_size_kb": pw_kb,
+            "fetch_factor_bytes_per_kb": f_factor,
+            "write_factor_bytes_per_kb": w_factor,
+        },
+    }
+    try:
+        table = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        table = {}
+    table[kernel_key] = rec
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return {kernel_key: rec}
+
+
+def trace_summary(kernel_trace_csv: str) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace CSV: per kernel and grid,
+    dispatch count and launch durations in microseconds."""
+    import statistics
+    groups, meta = {}, {}
+    for r in _csv_rows(kernel_trace_csv):
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        meta[key] = (r["VGPR_Count"], r["Accum_VGPR_Count"], r["SGPR_Count"], r["Scratch_Size"])
+    lines = ["| kernel | grid (work-items) | workgroup | dispatches | avg us | median us | min us "
+             "| max us | VGPR/AGPR/SGPR | scratch |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for key, d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        name = key[0].replace("|", "/")
+        name = name if len(name) <= 70 else name[:67] + "..."
+        v, a, sg, sc = meta[key]
+        lines.append(f"| {name} | {key[1]} | {key[2]} | {len(d)} | {statistics.mean(d):.1f} | "
+                     f"{statistics.median(d):.1f} | {min(d):.1f} | {max(d):.1f} | {v}/{a}/{sg} | {sc} |")
+    return "\n".join(lines)
 
 
 def main() -> int:
@@ -337,7 +489,22 @@ def main() -> int:
                          "(measured copy bandwidth of this GPU; the known-size kernel that "
                          "calibrates HBM traffic counters); 0 to skip")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn the counter_collection CSVs of two rocprofv3 passes "
+                         "(--pmc FETCH_SIZE, --pmc WRITE_SIZE) over this same command into "
+                         "calibrated HBM bytes per launch, recorded in profiles/traffic.json")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="no GPU: print a markdown table of a rocprofv3 kernel trace")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return 0
+    if args.ingest_counters:
+        rec = ingest_counters(*args.ingest_counters, W.get(args.workload), args.rank, args.state,
+                              args.probe_copy)
+        print(json.dumps(rec, indent=1))
+        return 0
 
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs one rank's shard step on one GPU; "
@@ -373,20 +540,21 @@ def main() -> int:
         step(t)
         t += 1
     stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: launch k's time is evs[k] -> evs[k+1]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for k in range(args.steps):
         step(t)
         t += 1
-    ev1.record(stream)
+        evs[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = wall * 1e3 / args.steps
     launches = len(sh.buckets) if args.bucket_params > 0 else 1
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps / launches   # average launch
+    step_ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps))
+    kernel_ms = evs[0].elapsed_time(evs[-1]) / args.steps / launches   # average launch
     ext = None
     if extended:
         # Time the final fused launch on its own (same state, next steps) so
@@ -444,8 +612,14 @@ def main() -> int:
     }
     if ext is not None:
         out["extended_reduce"] = ext
+    out["roofline"]["step_ms_median"] = step_ms[len(step_ms) // 2]
+    out["roofline"]["step_ms_min"] = step_ms[0]
     if args.probe_copy > 0:
         out["probe_copy"] = probe_copy(args.probe_copy)
+        out["probe_read"] = probe_read(args.probe_copy)
+        # the step's rate against the rates this GPU sustained on plain streams
+        out["roofline"]["vs_copy_probe"] = achieved / out["probe_copy"]["gbs"]
+        out["roofline"]["vs_read_probe"] = achieved / out["probe_read"]["gbs"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.rank, t, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -78,10 +78,11 @@ _lib.zero_reduce_shard.argtypes = [_vp, _i32, _i32, _i64, _vp, _vp]
 _lib.zero_adamw_shard.argtypes = [_vp, _vp, _vp, _vp, _i64, ctypes.POINTER(HParams), _vp]
 _lib.zero_gather_write.argtypes = [_vp, _i64, _vp, _i64, _vp]
 _lib.zero_probe_copy.argtypes = [_vp, _vp, _i64, _vp]
+_lib.zero_probe_read.argtypes = [_vp, _i64, _vp, ctypes.c_uint32, _vp]
 _lib.zero_strerror.argtypes = [_i32]
 _lib.zero_strerror.restype = ctypes.c_char_p
 for _f in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
-           "zero_gather_write", "zero_probe_copy", "zero_version", "zero_shard_step_ex",
+           "zero_gather_write", "zero_probe_copy", "zero_probe_read", "zero_version", "zero_shard_step_ex",
            "zero_accumulate_shard", "zero_shard_step_bf16_moments"):
     getattr(_lib, _f).restype = _i32
 
@@ -240,6 +241,11 @@ def zero_gather_write(master: Ptr, shard_len: int, d_chunks: Ptr, n_chunks: int,
 def zero_probe_copy(src: Ptr, dst: Ptr, nbytes: int, stream=None) -> None:
     _check(_lib.zero_probe_copy(_addr(src), _addr(dst), nbytes, _stream(stream)),
            "zero_probe_copy")
+
+
+def zero_probe_read(src: Ptr, nbytes: int, sink: Ptr, magic: int = 0x9E3779B9, stream=None) -> None:
+    _check(_lib.zero_probe_read(_addr(src), nbytes, _addr(sink), magic, _stream(stream)),
+           "zero_probe_read")
 
 
 def raw_call(name: str, *args) -> int:

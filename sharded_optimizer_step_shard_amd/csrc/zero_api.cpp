@@ -124,7 +124,7 @@ bool in_device_alloc(const void *p, int64_t bytes)
 
 extern "C" {
 
-int zero_version(void) { return (1 << 16) | 2; }
+int zero_version(void) { return (1 << 16) | 3; }
 
 const char *zero_strerror(int code)
 {
@@ -460,6 +460,19 @@ int zero_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t strea
     if (!in_device_alloc(src, bytes) || !in_device_alloc(dst, bytes))
         return ZERO_ERR_NOT_DEVICE;
     return hip_status(launch_probe_copy(src, dst, bytes, stream));
+}
+
+int zero_probe_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t magic, hipStream_t stream)
+{
+    if (((!src || !sink) && bytes > 0) || bytes < 0)
+        return ZERO_ERR_INVALID;
+    if (!aligned16(src) || ((uintptr_t)sink & 3u) != 0)
+        return ZERO_ERR_MISALIGNED;
+    if (bytes == 0)
+        return ZERO_OK;
+    if (!in_device_alloc(src, bytes) || !in_device_alloc(sink, 4))
+        return ZERO_ERR_NOT_DEVICE;
+    return hip_status(launch_probe_read(src, bytes, sink, magic, stream));
 }
 
 }  // extern "C"

@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
-                 "zero_gather_write", "zero_strerror", "zero_version", "zero_probe_copy"):
+                 "zero_gather_write", "zero_strerror", "zero_version", "zero_probe_copy",
+                 "zero_probe_read"):
         assert name in fns
 
 
@@ -48,7 +49,7 @@ def test_library_exports_every_declared_symbol(zs):
 
 
 def test_version_and_strerror(zs):
-    assert zs.zero_version() == (1, 2)
+    assert zs.zero_version() == (1, 3)
     for code in range(8):
         assert zs.zero_strerror(code) and zs.zero_strerror(code) != "unknown error code"
     assert zs.zero_strerror(99) == "unknown error code"
@@ -118,6 +119,7 @@ def test_non_device_addresses_are_rejected(zs):
     assert zs.raw_call("zero_gather_write", a, 10, a + 4096, 1, None) == zs.ZERO_ERR_NOT_DEVICE
     host = np.zeros(1024, np.float32)
     assert zs.raw_call("zero_probe_copy", host.ctypes.data, a, 1024, None) == zs.ZERO_ERR_NOT_DEVICE
+    assert zs.raw_call("zero_probe_read", host.ctypes.data, 1024, a, 0, None) == zs.ZERO_ERR_NOT_DEVICE
 
 
 def test_empty_calls_are_noops(zs):
@@ -130,6 +132,7 @@ def test_empty_calls_are_noops(zs):
     assert zs.raw_call("zero_adamw_shard", None, None, None, None, 0, ctypes.byref(hp), None) == 0
     assert zs.raw_call("zero_gather_write", None, 0, None, 0, None) == zs.ZERO_OK
     assert zs.raw_call("zero_probe_copy", None, None, 0, None) == zs.ZERO_OK
+    assert zs.raw_call("zero_probe_read", None, 0, None, 0, None) == zs.ZERO_OK
 
 
 def test_unfused_argument_errors(zs):
@@ -147,6 +150,10 @@ def test_unfused_argument_errors(zs):
     assert zs.raw_call("zero_gather_write", a + 8, 10, a + 4096, 1, None) == zs.ZERO_ERR_MISALIGNED
     assert zs.raw_call("zero_gather_write", a, -1, a + 4096, 1, None) == zs.ZERO_ERR_INVALID
     assert zs.raw_call("zero_probe_copy", a, a + 64, 128, None) == zs.ZERO_ERR_ALIAS
+    assert zs.raw_call("zero_probe_read", a, -16, a, 0, None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_probe_read", a, 64, None, 0, None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_probe_read", a + 8, 64, a, 0, None) == zs.ZERO_ERR_MISALIGNED
+    assert zs.raw_call("zero_probe_read", a, 64, a + 2, 0, None) == zs.ZERO_ERR_MISALIGNED
 
 
 # ---------------------------------------------------------------- chunk table

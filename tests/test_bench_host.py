@@ -33,3 +33,61 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def _write_counter_csv(path, counter, rows):
+    cols = ["Correlation_Id", "Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(path, "w") as f:
+        f.write(",".join(f'"{c}"' for c in cols) + "\n")
+        for i, (name, grid, value) in enumerate(rows):
+            f.write(f'{i},{i},{grid},"{name}","{counter}",{value}\n')
+
+
+def test_ingest_counters_calibrates_against_the_copy(tmp_path, monkeypatch):
+    """Counter KiB are scaled by the copy kernel's known bytes; only the step
+    kernel's largest-grid dispatches count (the warm-start prefix launches
+    have a smaller grid); the record lands under the source hash."""
+    from synth import workloads as W
+    w = W.get("gpt2")
+    lo, hi = w.shard_range(0)
+    n = hi - lo
+    probe = 1 << 30
+    step = "void zs::shard_step_kernel<(zero_dtype)0, 8, false, -1>(zs::StepArgs)"
+    copy = "zs::probe_copy_kernel(unsigned int __vector(4) const*)"
+    # the copy reads probe bytes as probe/2048 units, writes probe/1024 units
+    fetch_kb = (2 * n * 8 + 12 * n) / 2048.0
+    write_kb = 14 * n / 1024.0
+    _write_counter_csv(tmp_path / "f.csv", "FETCH_SIZE",
+                       [(step, 4096, 1.0), (step, 999424, fetch_kb), (step, 999424, fetch_kb * 1.01),
+                        (copy, 65536, probe / 2048.0), (copy, 65536, probe / 2048.0)])
+    _write_counter_csv(tmp_path / "w.csv", "WRITE_SIZE",
+                       [(step, 4096, 1.0), (step, 999424, write_kb), (step, 999424, write_kb),
+                        (copy, 65536, probe / 1024.0)])
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    rec = bench.ingest_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), w, 0, "fp32", probe)
+    r = rec[f"shard_step_kernel<bf16,8>/{w.name}"]
+    assert r["calibration"]["fetch_factor_bytes_per_kb"] == 2048.0
+    assert r["calibration"]["write_factor_bytes_per_kb"] == 1024.0
+    assert r["algorithmic_read_bytes"] == 28 * n and r["algorithmic_write_bytes"] == 14 * n
+    assert r["fetch_over_algorithmic"] == pytest.approx(1.005)
+    assert r["write_over_algorithmic"] == pytest.approx(1.0)
+    assert r["dispatches"] == [2, 2] and r["grid"] == 999424
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: r["source_hash"])
+    assert bench.load_traffic(f"shard_step_kernel<bf16,8>/{w.name}")["bytes_per_launch"] == r["bytes_per_launch"]
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "another source")
+    assert bench.load_traffic(f"shard_step_kernel<bf16,8>/{w.name}") is None
+
+
+def test_trace_summary_groups_by_kernel_and_grid(tmp_path):
+    cols = ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp",
+            "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Scratch_Size"]
+    rows = [("k_a", 64, 64, 0, 1000), ("k_a", 64, 64, 5000, 8000), ("k_a", 128, 64, 0, 500),
+            ("k_b", 256, 256, 0, 100)]
+    with open(tmp_path / "t.csv", "w") as f:
+        f.write(",".join(cols) + "\n")
+        for name, g, wg, s, e in rows:
+            f.write(f"{name},{g},{wg},{s},{e},8,0,16,0\n")
+    lines = bench.trace_summary(str(tmp_path / "t.csv")).splitlines()
+    assert lines[2].startswith("| k_a | 64 | 64 | 2 | 2.0 | 2.0 | 1.0 | 3.0 |")
+    assert lines[3].startswith("| k_a | 128 | 64 | 1 | 0.5 |")
+    assert lines[4].startswith("| k_b | 256 | 256 | 1 | 0.1 |")
