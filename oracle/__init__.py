@@ -59,6 +59,9 @@ def _load(path: str):
     L.oracle_bf16_from_double_array.argtypes = [vp, i64, vp]
     L.oracle_shard_step_bf16m.argtypes = [vp, i32, i32, i64, vp, vp, vp,
                                           ctypes.POINTER(HParams), vp]
+    L.oracle_kahan_add.argtypes = [vp, vp, vp, i64]
+    L.oracle_shard_step_kahan.argtypes = [vp, i32, i32, i64, vp, vp, vp, vp,
+                                          ctypes.POINTER(HParams)]
     L.oracle_shard_segments.argtypes = [vp, i32, i32, i32, vp, i64, ctypes.POINTER(i64)]
     L.oracle_shard_segments.restype = i64
     L.oracle_set_threads.argtypes = [i32]
@@ -66,7 +69,7 @@ def _load(path: str):
     for f in (L.oracle_bf16_round_array, L.oracle_reduce, L.oracle_adamw,
               L.oracle_shard_step, L.oracle_set_threads, L.oracle_reduce_ex,
               L.oracle_accumulate, L.oracle_shard_step_ex, L.oracle_bf16_from_double_array,
-              L.oracle_shard_step_bf16m):
+              L.oracle_shard_step_bf16m, L.oracle_kahan_add, L.oracle_shard_step_kahan):
         f.restype = None
     return L
 
@@ -214,6 +217,31 @@ def shard_step_bf16m(partials: Sequence[np.ndarray], master, m_bits, v_bits, hp:
     lib().oracle_shard_step_bf16m(_ptr_array(partials), len(partials), _gdt(partials), n,
                                   _p(th), _p(mm), _p(vv), ctypes.byref(hp), _p(prm))
     return th, mm, vv, prm
+
+
+def kahan_add(theta_bits, comp_bits, delta):
+    """Compensated add of float64 increments into bf16 (theta, comp) pairs
+    (uint16 bit patterns); returns the new (theta_bits, comp_bits)."""
+    th = np.array(theta_bits, dtype=np.uint16, copy=True)
+    c = np.array(comp_bits, dtype=np.uint16, copy=True)
+    d = np.ascontiguousarray(np.broadcast_to(np.asarray(delta, dtype=np.float64), th.shape))
+    lib().oracle_kahan_add(_p(th), _p(c), _p(d), th.size)
+    return th, c
+
+
+def shard_step_kahan(partials: Sequence[np.ndarray], theta_bits, comp_bits, m_bits, v_bits,
+                     hp: HParams):
+    """Shard step on the pure-bf16 state with the compensated update: the
+    parameters (shard order), compensation, m and v as uint16 bf16 bits;
+    returns the new (theta, comp, m, v) bits."""
+    n = len(theta_bits)
+    th = np.array(theta_bits, dtype=np.uint16, copy=True)
+    c = np.array(comp_bits, dtype=np.uint16, copy=True)
+    mm = np.array(m_bits, dtype=np.uint16, copy=True)
+    vv = np.array(v_bits, dtype=np.uint16, copy=True)
+    lib().oracle_shard_step_kahan(_ptr_array(partials), len(partials), _gdt(partials), n,
+                                  _p(th), _p(c), _p(mm), _p(vv), ctypes.byref(hp))
+    return th, c, mm, vv
 
 
 def shard_segments(numels: Sequence[int], n_ranks: int, rank: int) -> Tuple[np.ndarray, int]:

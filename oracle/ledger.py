@@ -50,6 +50,10 @@ MIXED_PRECISION_ADAM = Ledger(param=2, grad=2, optimizer=4 + 4 + 4)
 # Everything but the fp32 master in bf16: 2 + 2 + (4 master + 2 m + 2 v).
 BF16_MOMENTS_ADAM = Ledger(param=2, grad=2, optimizer=4 + 2 + 2)
 
+# Pure bf16 with a compensated update: bf16 parameter (the only weight copy),
+# gradient, m, v and Kahan compensation; no fp32 master.
+PURE_BF16_KAHAN = Ledger(param=2, grad=2, optimizer=2 + 2 + 2)
+
 # Element sizes of the arrays the shard step reads and writes: bf16 param
 # slot, bf16 gradient partial, fp32 master, fp32 m, fp32 v.
 STATE_ELEMENT_BYTES = {"param": 2, "grad": 2, "master": 4, "m": 4, "v": 4}
@@ -61,3 +65,10 @@ def shard_step_bytes_per_param(n_ranks: int, grad_bytes: int = 2, moment_bytes: 
     parameter.  moment_bytes = 2 for the 12-byte ledger's bf16 moments."""
     s = STATE_ELEMENT_BYTES
     return n_ranks * grad_bytes + 2 * (s["master"] + 2 * moment_bytes) + s["param"]
+
+
+def kahan_step_bytes_per_param(n_ranks: int, grad_bytes: int = 2) -> int:
+    """HBM bytes of the fused pure-bf16 step per shard element: N gradient
+    partials read; parameter, compensation, m, v (bf16 each) read and
+    written."""
+    return n_ranks * grad_bytes + 2 * (2 + 2 + 2 + 2)

@@ -59,6 +59,10 @@
 
 enum { ORACLE_BF16 = 0, ORACLE_FP32 = 1 };
 
+/* Loops over fewer elements than this run on the calling thread (elements
+ * are independent, so the split never changes a result). */
+#define ORACLE_PAR_MIN 16384
+
 typedef struct {
     double lr, beta1, beta2, eps, weight_decay;
     int64_t step; /* t >= 1: the number of this update, counted from 1 */
@@ -97,7 +101,7 @@ uint16_t oracle_bf16_round(float x)
 
 void oracle_bf16_round_array(const float *in, int64_t n, uint16_t *out)
 {
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n > ORACLE_PAR_MIN)
     for (int64_t i = 0; i < n; ++i)
         out[i] = oracle_bf16_round(in[i]);
 }
@@ -226,7 +230,7 @@ uint16_t oracle_bf16_from_double(double d)
 
 void oracle_bf16_from_double_array(const double *in, int64_t n, uint16_t *out)
 {
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n > ORACLE_PAR_MIN)
     for (int64_t i = 0; i < n; ++i)
         out[i] = oracle_bf16_from_double(in[i]);
 }
@@ -236,7 +240,7 @@ void oracle_bf16_from_double_array(const double *in, int64_t n, uint16_t *out)
 /* g_out[i] = fp32( (p_0[i] + p_1[i] + ... + p_{N-1}[i]) / N ), i in [0, n). */
 void oracle_reduce(const void *const *partials, int n_ranks, int gdt, int64_t n, float *g_out)
 {
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n > ORACLE_PAR_MIN)
     for (int64_t i = 0; i < n; ++i)
         g_out[i] = reduce_one(partials, n_ranks, gdt, i);
 }
@@ -247,7 +251,7 @@ void oracle_adamw(const float *g, float *master, float *m, float *v, int64_t n,
 {
     double bc1 = bias_correction(hp->beta1, hp->step);
     double bc2 = bias_correction(hp->beta2, hp->step);
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n > ORACLE_PAR_MIN)
     for (int64_t i = 0; i < n; ++i)
         adamw_one(g[i], &master[i], &m[i], &v[i], hp, bc1, bc2);
 }
@@ -259,7 +263,7 @@ void oracle_shard_step(const void *const *partials, int n_ranks, int gdt, int64_
 {
     double bc1 = bias_correction(hp->beta1, hp->step);
     double bc2 = bias_correction(hp->beta2, hp->step);
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n > ORACLE_PAR_MIN)
     for (int64_t i = 0; i < n; ++i) {
         float g = reduce_one(partials, n_ranks, gdt, i);
         adamw_one(g, &master[i], &m[i], &v[i], hp, bc1, bc2);
@@ -272,7 +276,7 @@ void oracle_shard_step(const void *const *partials, int n_ranks, int gdt, int64_
 void oracle_reduce_ex(const void *const *partials, int n_ranks, int group, int gdt,
                       const float *acc, int64_t micro_batches, int64_t n, float *g_out)
 {
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n > ORACLE_PAR_MIN)
     for (int64_t i = 0; i < n; ++i)
         g_out[i] = reduce_ex_one(partials, n_ranks, group, gdt, acc, micro_batches, i);
 }
@@ -281,7 +285,7 @@ void oracle_reduce_ex(const void *const *partials, int n_ranks, int group, int g
 void oracle_accumulate(const void *const *partials, int n_ranks, int group, int gdt,
                        int64_t n, float *acc, int reset)
 {
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n > ORACLE_PAR_MIN)
     for (int64_t i = 0; i < n; ++i) {
         double s = grouped_sum(partials, n_ranks, group, gdt, i);
         acc[i] = reset ? (float)s : (float)((double)acc[i] + s);
@@ -295,7 +299,7 @@ void oracle_shard_step_ex(const void *const *partials, int n_ranks, int group, i
 {
     double bc1 = bias_correction(hp->beta1, hp->step);
     double bc2 = bias_correction(hp->beta2, hp->step);
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n > ORACLE_PAR_MIN)
     for (int64_t i = 0; i < n; ++i) {
         float g = reduce_ex_one(partials, n_ranks, group, gdt, acc, micro_batches, i);
         adamw_one(g, &master[i], &m[i], &v[i], hp, bc1, bc2);
@@ -311,7 +315,7 @@ void oracle_shard_step_bf16m(const void *const *partials, int n_ranks, int gdt, 
 {
     double bc1 = bias_correction(hp->beta1, hp->step);
     double bc2 = bias_correction(hp->beta2, hp->step);
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n > ORACLE_PAR_MIN)
     for (int64_t i = 0; i < n; ++i) {
         double g = reduce_one(partials, n_ranks, gdt, i);
         double m1 = hp->beta1 * bf16_value(m[i]) + (1.0 - hp->beta1) * g;
@@ -325,6 +329,62 @@ void oracle_shard_step_bf16m(const void *const *partials, int n_ranks, int gdt, 
         master[i] = (float)th;
         if (param_out)
             param_out[i] = oracle_bf16_round(master[i]);
+    }
+}
+
+/*
+ * Pure-bf16 state with a compensated parameter update.  Lecture 8, Slide 28
+ * sizes its ZeRO capacity table with a "pure-BF16/Kahan" ledger and gives
+ * no formula.  Reading: the bf16 parameter (in its slot) is the only copy
+ * of the weight, there is no fp32 master; a bf16 buffer c holds the part of
+ * earlier increments that the bf16 parameter has not absorbed yet.  The
+ * increment is added by Kahan's compensated summation (Kahan 1965; applied
+ * to bf16 weight updates by Zamirai et al., "Revisiting BFloat16 Training"):
+ *     y      = d + c
+ *     theta' = bf16(theta + y)
+ *     c'     = bf16(y - (theta' - theta))
+ * with d the AdamW increment -lr (u + wd theta), u = mhat / (sqrt(vhat) + eps)
+ * from bf16 m, v as in the 12-byte step.  Arithmetic in double; each stored
+ * value (theta', c', m', v') is rounded once to nearest-even bf16.
+ */
+static void kahan_one(uint16_t *theta, uint16_t *comp, double d)
+{
+    double th = bf16_value(*theta);
+    double y = d + bf16_value(*comp);
+    uint16_t t1 = oracle_bf16_from_double(th + y);
+    double moved = bf16_value(t1) - th;           /* what theta absorbed */
+    *comp = oracle_bf16_from_double(y - moved);
+    *theta = t1;
+}
+
+/* The compensated add alone: (theta, c) += delta, element by element. */
+void oracle_kahan_add(uint16_t *theta, uint16_t *comp, const double *delta, int64_t n)
+{
+#pragma omp parallel for schedule(static) if (n > ORACLE_PAR_MIN)
+    for (int64_t i = 0; i < n; ++i)
+        kahan_one(&theta[i], &comp[i], delta[i]);
+}
+
+/* The shard step on the pure-bf16 state: theta (the parameters in shard
+ * order), comp, m, v are bf16 bit patterns, updated in place. */
+void oracle_shard_step_kahan(const void *const *partials, int n_ranks, int gdt, int64_t n,
+                             uint16_t *theta, uint16_t *comp, uint16_t *m, uint16_t *v,
+                             const oracle_hparams *hp)
+{
+    double bc1 = bias_correction(hp->beta1, hp->step);
+    double bc2 = bias_correction(hp->beta2, hp->step);
+#pragma omp parallel for schedule(static) if (n > ORACLE_PAR_MIN)
+    for (int64_t i = 0; i < n; ++i) {
+        double g = reduce_one(partials, n_ranks, gdt, i);
+        double m1 = hp->beta1 * bf16_value(m[i]) + (1.0 - hp->beta1) * g;
+        double v1 = hp->beta2 * bf16_value(v[i]) + (1.0 - hp->beta2) * (g * g);
+        double mhat = m1 / bc1;
+        double vhat = v1 / bc2;
+        double upd = mhat / (sqrt(vhat) + hp->eps);
+        double d = -hp->lr * (upd + hp->weight_decay * bf16_value(theta[i]));
+        m[i] = oracle_bf16_from_double(m1);
+        v[i] = oracle_bf16_from_double(v1);
+        kahan_one(&theta[i], &comp[i], d);
     }
 }
 

@@ -16,6 +16,7 @@ import oracle
 import test_oracle_pins as pins
 import test_oracle_pins_ex as pins_ex
 import test_oracle_pins_bf16m as pins_m
+import test_oracle_pins_kahan as pins_k
 
 MUTANTS = {
     "drop_last_rank": ("for (int k = 1; k < n_ranks; ++k)", "for (int k = 1; k < n_ranks - 1; ++k)"),
@@ -56,6 +57,19 @@ MUTANTS = {
     "bf16m_v_from_m": ("v[i] = oracle_bf16_from_double(v1);", "v[i] = oracle_bf16_from_double(m1);"),
     "bf16m_beta_swapped": ("hp->beta1 * bf16_value(m[i]) + (1.0 - hp->beta1) * g",
                            "(1.0 - hp->beta1) * bf16_value(m[i]) + hp->beta1 * g"),
+    "kahan_comp_ignored": ("double y = d + bf16_value(*comp);", "double y = d;"),
+    "kahan_comp_sign": ("double y = d + bf16_value(*comp);", "double y = d - bf16_value(*comp);"),
+    "kahan_residual_sign": ("*comp = oracle_bf16_from_double(y - moved);",
+                            "*comp = oracle_bf16_from_double(moved - y);"),
+    "kahan_comp_reset": ("*comp = oracle_bf16_from_double(y - moved);", "*comp = 0;"),
+    "kahan_theta_via_fp32": ("uint16_t t1 = oracle_bf16_from_double(th + y);",
+                             "uint16_t t1 = oracle_bf16_round((float)(th + y));"),
+    "kahan_decay_dropped": ("(upd + hp->weight_decay * bf16_value(theta[i]))", "(upd)"),
+    "kahan_decay_unscaled": ("-hp->lr * (upd + hp->weight_decay * bf16_value(theta[i]))",
+                             "-(hp->lr * upd + hp->weight_decay * bf16_value(theta[i]))"),
+    "kahan_update_sign": ("double d = -hp->lr * (upd", "double d = hp->lr * (upd"),
+    "kahan_moment_from_theta": ("double m1 = hp->beta1 * bf16_value(m[i]) + (1.0 - hp->beta1) * g;\n        double v1 = hp->beta2 * bf16_value(v[i]) + (1.0 - hp->beta2) * (g * g);\n        double mhat = m1 / bc1;\n        double vhat = v1 / bc2;\n        double upd = mhat / (sqrt(vhat) + hp->eps);\n        double d",
+                                "double m1 = hp->beta1 * bf16_value(m[i]) + (1.0 - hp->beta1) * g;\n        double v1 = hp->beta2 * bf16_value(m[i]) + (1.0 - hp->beta2) * (g * g);\n        double mhat = m1 / bc1;\n        double vhat = v1 / bc2;\n        double upd = mhat / (sqrt(vhat) + hp->eps);\n        double d"),
     "accumulate_rounds_twice": ("acc[i] = reset ? (float)s : (float)((double)acc[i] + s);",
                                 "acc[i] = reset ? (float)s : (float)((double)acc[i] + (double)(float)s);"),
 }
@@ -82,6 +96,12 @@ FAST_PINS = [
     lambda: pins_m.test_bf16_moment_step_equals_fp32_step_when_moments_are_exact(),
     lambda: pins_m.test_bf16_moment_step_rounds_moments_to_nearest(),
     lambda: pins_m.test_bf16_moment_step_rounds_once(),
+    lambda: pins_k.test_compensation_recovers_increments_a_bf16_sum_drops(),
+    lambda: pins_k.test_no_increment_is_lost_while_the_residual_fits(0, K=60),
+    lambda: pins_k.test_each_stored_value_is_the_nearest_bf16(n=400),
+    lambda: pins_k.test_pure_decay_is_followed_where_plain_bf16_stalls(),
+    lambda: pins_k.test_first_step_closed_form(n=400),
+    lambda: pins_k.test_moments_are_those_of_the_bf16_moment_step(),
 ]
 
 
