@@ -40,6 +40,16 @@ KERNEL_SOURCES = [os.path.join(ROOT, "sharded_optimizer_step_shard_amd", "csrc",
                   for f in ("zero_kernels.hip", "zero_api.cpp", "zero_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
+# Optimizer-state layouts the fused step runs on: the kernel, the state bytes
+# read and written per shard element besides the N gradient partials, and a
+# description.
+STATES = {
+    "fp32": ("shard_step_kernel", 12, 14, "fp32 master, m, v; bf16 parameter written"),
+    "bf16-moments": ("shard_step_m16_kernel", 8, 10, "fp32 master, bf16 m, v; bf16 parameter written"),
+    "bf16-kahan": ("shard_step_kahan_kernel", 8, 8,
+                   "bf16 parameter (read and written in place), bf16 Kahan compensation, m, v"),
+}
+
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
@@ -163,6 +173,26 @@ class Shard:
         self.v = self.v.to(torch.bfloat16).view(torch.int16).contiguous()
         self.state = "bf16-moments"
 
+    def use_kahan(self) -> None:
+        """Switch to the pure-bf16 state: the bf16 parameters at the chunks'
+        destinations become the weights (written from the current fp32 master
+        by the library's bf16 write), with a zero Kahan compensation and the
+        moments rounded to bf16 with torch.  Set-up only; the fp32 master is
+        released."""
+        import torch
+        self.zs.zero_gather_write(self.master, self.n, self.d_table, len(self.table))
+        self.comp = torch.zeros(self.n, dtype=torch.int16, device=self.dev)
+        self.m = self.m.to(torch.bfloat16).view(torch.int16).contiguous()
+        self.v = self.v.to(torch.bfloat16).view(torch.int16).contiguous()
+        self.master = None
+        self.state = "bf16-kahan"
+
+    def step_kahan(self, t: int) -> None:
+        self.zs.zero_shard_step_kahan(self.partials, self.comp, self.m, self.v, self.n,
+                                      self.d_table, len(self.table),
+                                      self.zs.hparams(t, **self.w.hparams()))
+        self.step_t = t
+
     def step_bf16_moments(self, t: int) -> None:
         self.zs.zero_shard_step_bf16_moments(self.partials, self.master, self.m, self.v, self.n,
                                              self.d_table, len(self.table),
@@ -223,8 +253,8 @@ class Shard:
         return out
 
     def bytes_per_launch(self) -> int:
-        moments = 8 if getattr(self, "state", "fp32") == "fp32" else 4
-        return (self.w.bytes_per_param() - 2 * (8 - moments)) * self.n
+        _, rd, wr, _ = STATES[getattr(self, "state", "fp32")]
+        return (self.w.n_ranks * (2 if self.w.gdt == "bf16" else 4) + rd + wr) * self.n
 
 
 def bucket_runs(chunk_lens, bucket_params: int) -> list:
@@ -247,9 +277,11 @@ def bucket_runs(chunk_lens, bucket_params: int) -> list:
 
 
 def cpu_baseline(w: W.Workload, rank: int, t: int, target_s: float = 10.0,
-                 sample: int = 1 << 22) -> dict:
-    """The CPU oracle on a bounded sample (the first `sample` shard elements)
-    of the same workload, repeated until ~target_s of work; params/s."""
+                 sample: int = 1 << 22, state: str = "fp32") -> dict:
+    """The CPU oracle of the same step (the same state layout) on a bounded
+    sample (the first `sample` shard elements) of the same workload,
+    repeated until ~target_s of work; params/s.  Then the same on one
+    thread over a quarter of the sample."""
     import oracle
 
     lo, hi = w.shard_range(rank)
@@ -258,39 +290,45 @@ def cpu_baseline(w: W.Workload, rank: int, t: int, target_s: float = 10.0,
                         w.sigma_grad, synth.stream_id(synth.KIND_OUTLIER, k, t),
                         w.outlier_frac, w.outlier_mult) for k in range(w.n_ranks)]
     master = synth.fill("f32", w.seed, synth.stream_id(synth.KIND_MASTER), lo, n, w.sigma_master)
-    m = np.zeros(n, np.float32)
-    v = np.zeros(n, np.float32)
-    done, elapsed, reps = 0, 0.0, 0
-    while elapsed < target_s:
-        t0 = time.perf_counter()
-        oracle.shard_step(parts, master, m, v, oracle.hparams(t + reps, **w.hparams()),
-                          in_place=True)
-        elapsed += time.perf_counter() - t0
-        done += n
-        reps += 1
-    # the same oracle on one thread, on a quarter of the sample
+    zero16 = np.zeros(n, np.uint16)
+
+    def run(k: int, budget: float) -> tuple:
+        """Oracle steps over the first k elements until `budget` seconds."""
+        sub = [p[:k] for p in parts]
+        th, m, v = master[:k].copy(), np.zeros(k, np.float32), np.zeros(k, np.float32)
+        th16, c16 = oracle.bf16_round(th), zero16[:k].copy()
+        m16, v16 = zero16[:k].copy(), zero16[:k].copy()
+        done, elapsed, reps = 0, 0.0, 0
+        while elapsed < budget:
+            hp = oracle.hparams(t + reps, **w.hparams())
+            t0 = time.perf_counter()
+            if state == "fp32":
+                oracle.shard_step(sub, th, m, v, hp, in_place=True)
+            elif state == "bf16-moments":
+                th, m16, v16, _ = oracle.shard_step_bf16m(sub, th, m16, v16, hp)
+            else:
+                th16, c16, m16, v16 = oracle.shard_step_kahan(sub, th16, c16, m16, v16, hp)
+            elapsed += time.perf_counter() - t0
+            done += k
+            reps += 1
+        return done / elapsed, reps, elapsed
+
     cores = oracle.max_threads()
+    value, reps, elapsed = run(n, target_s)
     n1 = max(1, n // 4)
     oracle.set_threads(1)
     try:
-        sub = [p[:n1] for p in parts]
-        done1, elapsed1, reps1 = 0, 0.0, 0
-        while elapsed1 < target_s / 4:
-            t0 = time.perf_counter()
-            oracle.shard_step(sub, master[:n1].copy(), m[:n1].copy(), v[:n1].copy(),
-                              oracle.hparams(t + reps1, **w.hparams()), in_place=True)
-            elapsed1 += time.perf_counter() - t0
-            done1 += n1
-            reps1 += 1
+        value1, reps1, elapsed1 = run(n1, target_s / 4)
     finally:
         oracle.set_threads(cores)
-    value = done / elapsed
+    _, rd, wr, _ = STATES[state]
+    bpp = w.n_ranks * (2 if w.gdt == "bf16" else 4) + rd + wr
     return {"value": value, "unit": "params/s", "cores": cores,
             "kind": "oracle",
             "sample": f"first {n} elements of rank {rank}'s shard of {w.name}, N={w.n_ranks} "
-                      f"{w.gdt} partials, {reps} oracle steps in {elapsed:.1f} s",
-            "host_gbs": value * w.bytes_per_param() / 1e9,
-            "single_thread": {"value": done1 / elapsed1, "unit": "params/s",
+                      f"{w.gdt} partials, {state} state, {reps} oracle steps in {elapsed:.1f} s",
+            "host_gbs": value * bpp / 1e9,
+            "single_thread": {"value": value1, "unit": "params/s",
                               "sample": f"first {n1} elements, {reps1} steps in {elapsed1:.1f} s"},
             "cpu_model": cpu_model()}
 
@@ -396,7 +434,7 @@ def ingest_counters(fetch_csv: str, write_csv: str, w: "W.Workload", rank: int, 
     bytes.  Records the result in profiles/traffic.json under the kernel
     source's hash (bench reports it as roofline.traffic only while the
     source is unchanged) and returns the record."""
-    kname = "shard_step_m16_kernel" if state == "bf16-moments" else "shard_step_kernel"
+    kname, rd, wr, _ = STATES[state]
     kernel_key = f"{kname}<{w.gdt},{w.n_ranks}>/{w.name}"
     f_kb, f_n, grid = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", kname)
     w_kb, w_n, _ = _counter_per_dispatch(write_csv, "WRITE_SIZE", kname)
@@ -405,9 +443,8 @@ def ingest_counters(fetch_csv: str, write_csv: str, w: "W.Workload", rank: int, 
     f_factor, w_factor = probe_bytes / pf_kb, probe_bytes / pw_kb
     lo, hi = w.shard_range(rank)
     n = hi - lo
-    mb = 4 if state == "fp32" else 2
-    alg_read = (w.n_ranks * (2 if w.gdt == "bf16" else 4) + 4 + 2 * mb) * n
-    alg_write = (4 + 2 * mb + 2) * n
+    alg_read = (w.n_ranks * (2 if w.gdt == "bf16" else 4) + rd) * n
+    alg_write = wr * n
     rec = {
         "source_hash": kernel_source_hash(),
         "bytes_per_launch": f_kb * f_factor + w_kb * w_factor,
@@ -474,9 +511,10 @@ def main() -> int:
     ap.add_argument("--max-chunk", type=int, default=None,
                     help="chunk-table cut length (default: the library's tuned value)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--state", default="fp32", choices=["fp32", "bf16-moments"],
-                    help="optimizer state: fp32 master, m, v (16 B/param ledger) or fp32 "
-                         "master with bf16 m, v (12 B/param ledger)")
+    ap.add_argument("--state", default="fp32", choices=sorted(STATES),
+                    help="optimizer state: fp32 master, m, v (16 B/param ledger); fp32 "
+                         "master with bf16 m, v (12 B/param ledger); or pure bf16 with a "
+                         "Kahan-compensated update (no master, 10 B/param)")
     ap.add_argument("--group", type=int, default=0,
                     help="two-level reduce: ranks per group (hybrid sharding); 0 = flat")
     ap.add_argument("--micro-batches", type=int, default=1,
@@ -525,11 +563,15 @@ def main() -> int:
     extended = args.group > 0 or args.micro_batches > 1
     if extended and args.bucket_params > 0:
         raise SystemExit("--bucket-params does not combine with --group/--micro-batches")
-    if args.state == "bf16-moments":
+    if args.state != "fp32":
         if extended or args.bucket_params > 0:
-            raise SystemExit("--state bf16-moments runs the plain fused step only")
-        sh.use_bf16_moments()
-        step = sh.step_bf16_moments
+            raise SystemExit(f"--state {args.state} runs the plain fused step only")
+        if args.state == "bf16-moments":
+            sh.use_bf16_moments()
+            step = sh.step_bf16_moments
+        else:
+            sh.use_kahan()
+            step = sh.step_kahan
     if args.bucket_params > 0:
         sh.set_buckets(args.bucket_params)
         step = sh.step_bucketed
@@ -579,7 +621,7 @@ def main() -> int:
     if extended and args.micro_batches > 1:
         bytes_launch += 4 * sh.n           # the accumulator read by the fused launch
     achieved = bytes_launch / (kernel_ms * 1e-3) / 1e9
-    kname = "shard_step_m16_kernel" if args.state == "bf16-moments" else "shard_step_kernel"
+    kname = STATES[args.state][0]
     kernel_key = f"{kname}<{w.gdt},{w.n_ranks}{',ext' if extended else ''}>/{w.name}"
     traffic = load_traffic(kernel_key) if launches == 1 else None
     out = {
@@ -597,7 +639,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{w.name} rank-{args.rank} shard", "shard_params": sh.n,
                    "n_ranks": w.n_ranks, "grad_dtype": w.gdt,
-                   "state_dtype": "fp32" if args.state == "fp32" else "fp32 master, bf16 m/v",
+                   "state_dtype": STATES[args.state][3],
                    "param_dtype": "bf16", "tensors": len(w.numels), "chunks": len(sh.table),
                    "dst": sh.dst_mode, "bytes_per_param": sh.bytes_per_launch() // sh.n,
                    "state": args.state,
@@ -621,7 +663,7 @@ def main() -> int:
         out["roofline"]["vs_copy_probe"] = achieved / out["probe_copy"]["gbs"]
         out["roofline"]["vs_read_probe"] = achieved / out["probe_read"]["gbs"]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.rank, t, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.rank, t, args.cpu_seconds, state=args.state)
     print(json.dumps(out), flush=True)
     return 0
 

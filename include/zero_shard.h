@@ -227,6 +227,28 @@ int zero_shard_step_bf16_moments(const void *const *partials, int n_ranks, zero_
                                  const zero_adamw_hparams *hp, hipStream_t stream);
 
 /*
+ * The fused step on the pure-bf16 state with a compensated update ("CS336
+ * 2026 Lecture 8: Parallelism Basics", Slide 28 sizes its capacity table
+ * with a pure-BF16/Kahan ledger): no fp32 master.  The bf16 parameters are
+ * the weights: each chunk's dst holds the parameters of its shard elements
+ * and is read and written in place.  comp, m, v: device, shard_len bf16
+ * patterns each, in shard order, updated in place (comp starts at zero).
+ * Per element, with g and u = mhat / (sqrt(vhat) + eps) as in
+ * zero_shard_step_bf16_moments and theta the bf16 parameter:
+ *   d = -lr (u + weight_decay theta),  y = d + comp,
+ *   theta' = bf16(theta + y),  comp' = bf16(y - (theta' - theta)),
+ * Kahan's compensated summation of the increments into theta; arithmetic
+ * in double, every stored value rounded once to nearest-even bf16.  Moves
+ * 2N + 16 bytes per element (bf16 partials).  The chunk table must cover
+ * each shard element at most once (zero_build_chunks' tables do).  Errors
+ * as zero_shard_step_bf16_moments, with comp in place of master.
+ */
+int zero_shard_step_kahan(const void *const *partials, int n_ranks, zero_dtype gdt,
+                          uint16_t *comp, uint16_t *m, uint16_t *v, int64_t shard_len,
+                          const zero_chunk *d_chunks, int64_t n_chunks,
+                          const zero_adamw_hparams *hp, hipStream_t stream);
+
+/*
  * Reduce only: grad_out[i] = fp32((p_0[i] + ... + p_{N-1}[i]) / N),
  * i in [0, n), summed in double in rank order.  grad_out must not overlap
  * any partial (ALIAS).  n == 0 is a no-op.

@@ -74,6 +74,8 @@ _lib.zero_shard_step_ex.argtypes = [_vp, _i32, _i32, ctypes.POINTER(ReduceSpec),
 _lib.zero_accumulate_shard.argtypes = [_vp, _i32, _i32, _i32, _i64, _vp, _i32, _vp]
 _lib.zero_shard_step_bf16_moments.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64,
                                               ctypes.POINTER(HParams), _vp]
+_lib.zero_shard_step_kahan.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64,
+                                       ctypes.POINTER(HParams), _vp]
 _lib.zero_reduce_shard.argtypes = [_vp, _i32, _i32, _i64, _vp, _vp]
 _lib.zero_adamw_shard.argtypes = [_vp, _vp, _vp, _vp, _i64, ctypes.POINTER(HParams), _vp]
 _lib.zero_gather_write.argtypes = [_vp, _i64, _vp, _i64, _vp]
@@ -83,7 +85,7 @@ _lib.zero_strerror.argtypes = [_i32]
 _lib.zero_strerror.restype = ctypes.c_char_p
 for _f in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
            "zero_gather_write", "zero_probe_copy", "zero_probe_read", "zero_version", "zero_shard_step_ex",
-           "zero_accumulate_shard", "zero_shard_step_bf16_moments"):
+           "zero_accumulate_shard", "zero_shard_step_bf16_moments", "zero_shard_step_kahan"):
     getattr(_lib, _f).restype = _i32
 
 Ptr = Union[int, "torch.Tensor", None]  # noqa: F821
@@ -208,6 +210,18 @@ def zero_shard_step_bf16_moments(partials: Sequence[Ptr], master: Ptr, m: Ptr, v
                                              _addr(master), _addr(m), _addr(v), shard_len,
                                              _addr(d_chunks), n_chunks, ctypes.byref(hp),
                                              _stream(stream)), "zero_shard_step_bf16_moments")
+
+
+def zero_shard_step_kahan(partials: Sequence[Ptr], comp: Ptr, m: Ptr, v: Ptr, shard_len: int,
+                          d_chunks: Ptr, n_chunks: int, hp: HParams, gdt: Optional[int] = None,
+                          stream=None) -> None:
+    """Fused step on the pure-bf16 state: the bf16 parameters at the chunks'
+    destinations are read and written in place; comp (Kahan compensation),
+    m and v are bf16 bit patterns in shard order."""
+    gdt = _gdt_of(partials) if gdt is None else gdt
+    _check(_lib.zero_shard_step_kahan(_partial_array(partials), len(partials), gdt, _addr(comp),
+                                      _addr(m), _addr(v), shard_len, _addr(d_chunks), n_chunks,
+                                      ctypes.byref(hp), _stream(stream)), "zero_shard_step_kahan")
 
 
 def zero_accumulate_shard(partials: Sequence[Ptr], n: int, acc: Ptr, reset: bool,

@@ -50,6 +50,7 @@ StepScalars make_scalars(const zero_adamw_hparams *hp)
     k.eps = hp->eps;
     k.lr = hp->lr;
     k.dec = 1.0 - hp->lr * hp->weight_decay;
+    k.wd = hp->weight_decay;
     return k;
 }
 
@@ -124,7 +125,7 @@ bool in_device_alloc(const void *p, int64_t bytes)
 
 extern "C" {
 
-int zero_version(void) { return (1 << 16) | 3; }
+int zero_version(void) { return (1 << 16) | 4; }
 
 const char *zero_strerror(int code)
 {
@@ -220,7 +221,7 @@ int zero_shard_step(const void *const *partials, int n_ranks, zero_dtype gdt,
                     const zero_chunk *d_chunks, int64_t n_chunks,
                     const zero_adamw_hparams *hp, hipStream_t stream)
 {
-    StepArgs a;
+    StepArgs a{};
     int rc = check_partials(partials, n_ranks, gdt, shard_len, a.parts);
     if (rc)
         return rc;
@@ -261,7 +262,7 @@ int zero_shard_step_ex(const void *const *partials, int n_ranks, zero_dtype gdt,
                        int64_t shard_len, const zero_chunk *d_chunks, int64_t n_chunks,
                        const zero_adamw_hparams *hp, hipStream_t stream)
 {
-    StepArgs a;
+    StepArgs a{};
     int rc = check_partials(partials, n_ranks, gdt, shard_len, a.parts);
     if (rc)
         return rc;
@@ -308,7 +309,7 @@ int zero_shard_step_bf16_moments(const void *const *partials, int n_ranks, zero_
                                  const zero_chunk *d_chunks, int64_t n_chunks,
                                  const zero_adamw_hparams *hp, hipStream_t stream)
 {
-    StepArgs a;
+    StepArgs a{};
     int rc = check_partials(partials, n_ranks, gdt, shard_len, a.parts);
     if (rc)
         return rc;
@@ -341,7 +342,50 @@ int zero_shard_step_bf16_moments(const void *const *partials, int n_ranks, zero_
     a.n_chunks = n_chunks;
     a.shard_len = shard_len;
     a.acc = nullptr;
+    a.comp = nullptr;
     return hip_status(launch_step_m16(a, gdt, stream));
+}
+
+int zero_shard_step_kahan(const void *const *partials, int n_ranks, zero_dtype gdt,
+                          uint16_t *comp, uint16_t *m, uint16_t *v, int64_t shard_len,
+                          const zero_chunk *d_chunks, int64_t n_chunks,
+                          const zero_adamw_hparams *hp, hipStream_t stream)
+{
+    StepArgs a{};
+    int rc = check_partials(partials, n_ranks, gdt, shard_len, a.parts);
+    if (rc)
+        return rc;
+    if (((!comp || !m || !v) && shard_len > 0) || shard_len < 0 || n_chunks < 0 ||
+        n_chunks > INT32_MAX || (n_chunks > 0 && !d_chunks) || !valid_hparams(hp))
+        return ZERO_ERR_INVALID;
+    if (!aligned16(comp) || !aligned16(m) || !aligned16(v) || !aligned16(d_chunks))
+        return ZERO_ERR_MISALIGNED;
+    const int64_t hb = shard_len * 2, gb = shard_len * elem_bytes(gdt);
+    if (overlaps(comp, hb, m, hb) || overlaps(comp, hb, v, hb) || overlaps(m, hb, v, hb))
+        return ZERO_ERR_ALIAS;
+    for (int k = 0; k < n_ranks; ++k)
+        if (overlaps(partials[k], gb, comp, hb) || overlaps(partials[k], gb, m, hb) ||
+            overlaps(partials[k], gb, v, hb))
+            return ZERO_ERR_ALIAS;
+    if (n_chunks == 0 || shard_len == 0)
+        return ZERO_OK;
+    for (int k = 0; k < n_ranks; ++k)
+        if (!in_device_alloc(partials[k], gb))
+            return ZERO_ERR_NOT_DEVICE;
+    if (!in_device_alloc(comp, hb) || !in_device_alloc(m, hb) || !in_device_alloc(v, hb) ||
+        !in_device_alloc(d_chunks, n_chunks * (int64_t)sizeof(zero_chunk)))
+        return ZERO_ERR_NOT_DEVICE;
+    a.red = make_reduce(n_ranks);
+    a.k = make_scalars(hp);
+    a.master = nullptr;
+    a.m = (float *)m;        // the kernel reads these as 16-bit patterns
+    a.v = (float *)v;
+    a.comp = comp;
+    a.chunks = d_chunks;
+    a.n_chunks = n_chunks;
+    a.shard_len = shard_len;
+    a.acc = nullptr;
+    return hip_status(launch_step_kahan(a, gdt, stream));
 }
 
 int zero_accumulate_shard(const void *const *partials, int n_ranks, zero_dtype gdt, int group,

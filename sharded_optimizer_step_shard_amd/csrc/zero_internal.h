@@ -17,6 +17,7 @@ struct StepScalars {
     double bc1, bc2;   // 1 - beta1^t, 1 - beta2^t
     double eps, lr;
     double dec;        // 1 - lr * weight_decay
+    double wd;         // weight_decay
 };
 
 // Reduction constants: divide by the count (N, or N * micro-batches), or
@@ -44,6 +45,7 @@ struct StepArgs {
     int64_t n_chunks;
     int64_t shard_len;
     const float *acc;   // extended step: earlier micro-batches' sum, or null
+    uint16_t *comp;     // pure-bf16 step: Kahan compensation (bf16), or null
 };
 
 struct ReduceArgs {
@@ -78,6 +80,7 @@ struct GatherArgs {
 hipError_t launch_step(const StepArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_step_ex(const StepArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_step_m16(const StepArgs &a, zero_dtype gdt, hipStream_t s);
+hipError_t launch_step_kahan(const StepArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_accumulate(const AccArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs &a, hipStream_t s);

@@ -66,17 +66,25 @@ __device__ __forceinline__ float finish_reduce(double s, const ReduceScalars &r)
         return (float)(r.pow2 ? s * r.inv_n : s / r.n);
 }
 
-// AdamW on one element: moments in and out in double (the caller stores
-// them in their format), master in and out in fp32.
-__device__ __forceinline__ void adamw_d(float g32, float &th, double m0, double v0, double &m1,
-                                        double &v1, const StepScalars &k)
+// Adam's moments and update direction mhat / (sqrt(vhat) + eps) for one
+// element, all in double; the caller stores m1, v1 in their format.
+__device__ __forceinline__ double adam_dir(float g32, double m0, double v0, double &m1, double &v1,
+                                           const StepScalars &k)
 {
     double g = (double)g32;
     m1 = k.b1 * m0 + k.c1 * g;
     v1 = k.b2 * v0 + k.c2 * (g * g);
     double mhat = m1 / k.bc1;
     double vhat = v1 / k.bc2;
-    double upd = mhat / (__builtin_sqrt(vhat) + k.eps);
+    return mhat / (__builtin_sqrt(vhat) + k.eps);
+}
+
+// AdamW on one element: moments in and out in double (the caller stores
+// them in their format), master in and out in fp32.
+__device__ __forceinline__ void adamw_d(float g32, float &th, double m0, double v0, double &m1,
+                                        double &v1, const StepScalars &k)
+{
+    double upd = adam_dir(g32, m0, v0, m1, v1, k);
     double t1 = (double)th * k.dec - k.lr * upd;
     th = (float)t1;
 }
@@ -108,6 +116,28 @@ __device__ __forceinline__ uint32_t bf16_from_double(double d)
 }
 
 __device__ __forceinline__ double bf16_to_double(uint32_t h) { return (double)__uint_as_float(h << 16); }
+
+// One element of the pure-bf16 step: AdamW's increment -lr (u + wd theta)
+// added to the bf16 parameter by Kahan's compensated summation, the bf16
+// compensation c holding the part theta has not absorbed yet:
+//   y = d + c,  theta' = bf16(theta + y),  c' = bf16(y - (theta' - theta)).
+// Everything in double; each stored value (theta', c', m', v') is rounded
+// once to nearest-even bf16.  Bit patterns in and out.
+__device__ __forceinline__ void kahan_elem(float g32, uint32_t &th, uint32_t &c, uint32_t &m,
+                                           uint32_t &v, const StepScalars &k)
+{
+    double m1, v1;
+    const double upd = adam_dir(g32, bf16_to_double(m), bf16_to_double(v), m1, v1, k);
+    const double t0 = bf16_to_double(th);
+    const double d = -k.lr * (upd + k.wd * t0);
+    const double y = d + bf16_to_double(c);
+    const uint32_t t1 = bf16_from_double(t0 + y);
+    const double moved = bf16_to_double(t1) - t0;
+    c = bf16_from_double(y - moved);
+    th = t1;
+    m = bf16_from_double(m1);
+    v = bf16_from_double(v1);
+}
 
 template <typename T>
 __device__ __forceinline__ T ld(const T *p) { return *p; }
@@ -528,8 +558,83 @@ __device__ __forceinline__ void step_chunk_m16(const StepArgs &a, const zero_chu
     }
 }
 
+// Resident waves per SIMD of the 12-byte and pure-bf16 steps.  Both do more
+// arithmetic per byte moved than the 16-byte step (bf16 moments rounded from
+// double; the compensated update on top), and when the N partials are few
+// bytes per element one wave per SIMD leaves the memory pipe idle during its
+// arithmetic.  Measured on MI355X (7B shard, N = 8 bf16): the 12-byte step
+// 0.65 -> 0.67 of HBM peak with two waves, the pure-bf16 step 0.47 -> 0.655
+// with three; with 16 partials (70B) the 12-byte step is best with one wave
+// (0.725 against 0.69), the pure-bf16 step with two (0.63 -> 0.71; its
+// registers allow no third).
 template <zero_dtype G, int NC>
-__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+constexpr int kM16Waves = (NC > 0 && NC * Grad<G>::BYTES <= 16) ? 2 : 1;
+constexpr int kKahanWaves = 3;
+
+// The pure-bf16 step: the parameters are read from and written back to
+// the chunk's destination (the bf16 parameter is the only copy of the
+// weight), with bf16 compensation, m and v in shard order.
+template <zero_dtype G, int NC>
+__device__ __forceinline__ void step_chunk_kahan(const StepArgs &a, const zero_chunk &c)
+{
+    constexpr int VEC = Grad<G>::VEC;
+    if (c.len <= 0 || c.shard_off < 0 || c.shard_off > a.shard_len - c.len)
+        return;
+    const int n = NC > 0 ? NC : a.red.n_ranks;
+    uint16_t *const m16 = (uint16_t *)a.m, *const v16 = (uint16_t *)a.v, *const c16 = a.comp;
+    const int64_t lo = c.shard_off, hi = c.shard_off + c.len;
+    const int64_t g0 = lo / VEC, g1 = (hi + VEC - 1) / VEC;
+    const bool vec_ok = (((uintptr_t)c.dst - (uintptr_t)(2 * (lo - g0 * VEC))) % (2 * VEC)) == 0;
+    for (int64_t g = g0 + threadIdx.x; g < g1; g += kStepBlock) {
+        const int64_t i0 = g * VEC;
+        uint16_t *d = c.dst + (i0 - lo);
+        if (i0 >= lo && i0 + VEC <= hi) {
+            double s[VEC];
+            B16x<VEC> th, cm, m, v;
+            if (vec_ok) {
+                th.load(d);
+            } else {
+#pragma unroll
+                for (int j = 0; j < VEC; ++j)
+                    th.e[j] = d[j];
+            }
+            cm.load(c16 + i0);
+            m.load(m16 + i0);
+            v.load(v16 + i0);
+            group_sum<G, NC>(s, a.parts, n, i0);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+                kahan_elem(finish_reduce<NC>(s[j], a.red), th.e[j], cm.e[j], m.e[j], v.e[j], a.k);
+            cm.store(c16 + i0);
+            m.store(m16 + i0);
+            v.store(v16 + i0);
+            store_bf16<VEC>(d, th.e, vec_ok);
+        } else {
+            for (int j = 0; j < VEC; ++j) {
+                const int64_t i = i0 + j;
+                if (i < lo || i >= hi)
+                    continue;
+                uint32_t th = d[j], cm = c16[i], m = m16[i], v = v16[i];
+                kahan_elem(finish_reduce<NC>(elem_sum<G>(a.parts, n, i), a.red), th, cm, m, v, a.k);
+                d[j] = (uint16_t)th;
+                c16[i] = (uint16_t)cm;
+                m16[i] = (uint16_t)m;
+                v16[i] = (uint16_t)v;
+            }
+        }
+    }
+}
+
+template <zero_dtype G, int NC>
+__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, kKahanWaves)))
+void shard_step_kahan_kernel(StepArgs a)
+{
+    for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
+        step_chunk_kahan<G, NC>(a, chunk_at(a.chunks, ci));
+}
+
+template <zero_dtype G, int NC>
+__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, kM16Waves<G, NC>)))
 void shard_step_m16_kernel(StepArgs a)
 {
     for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
@@ -817,6 +922,28 @@ static hipError_t step_m16_dispatch(const StepArgs &a, hipStream_t s)
     default: hipLaunchKernelGGL((shard_step_m16_kernel<G, 0>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
+}
+
+template <zero_dtype G>
+static hipError_t step_kahan_dispatch(const StepArgs &a, hipStream_t s)
+{
+    const dim3 grid(chunk_grid(a.n_chunks)), block(kStepBlock);
+    switch (a.red.n_ranks) {
+    case 1: hipLaunchKernelGGL((shard_step_kahan_kernel<G, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((shard_step_kahan_kernel<G, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((shard_step_kahan_kernel<G, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((shard_step_kahan_kernel<G, 8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((shard_step_kahan_kernel<G, 16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((shard_step_kahan_kernel<G, 32>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((shard_step_kahan_kernel<G, 64>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((shard_step_kahan_kernel<G, 0>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_step_kahan(const StepArgs &a, zero_dtype gdt, hipStream_t s)
+{
+    return gdt == ZERO_BF16 ? step_kahan_dispatch<ZERO_BF16>(a, s) : step_kahan_dispatch<ZERO_FP32>(a, s);
 }
 
 hipError_t launch_step_m16(const StepArgs &a, zero_dtype gdt, hipStream_t s)

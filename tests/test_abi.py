@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
                  "zero_gather_write", "zero_strerror", "zero_version", "zero_probe_copy",
-                 "zero_probe_read"):
+                 "zero_probe_read", "zero_shard_step_kahan", "zero_shard_step_bf16_moments"):
         assert name in fns
 
 
@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol(zs):
 
 
 def test_version_and_strerror(zs):
-    assert zs.zero_version() == (1, 3)
+    assert zs.zero_version() == (1, 4)
     for code in range(8):
         assert zs.zero_strerror(code) and zs.zero_strerror(code) != "unknown error code"
     assert zs.zero_strerror(99) == "unknown error code"
@@ -104,6 +104,32 @@ def test_shard_step_argument_errors(zs):
                 n=1000) == E.ZERO_ERR_ALIAS
     assert step(zs, parts(4), 4, gdt=1, master=BASE + 3008, n=1000,
                 ) == E.ZERO_ERR_ALIAS   # fp32 partial 0 is 4000 bytes long
+
+
+def kahan(zs, p, n_ranks, gdt=0, comp=BASE + (1 << 40), m=BASE + (1 << 40) + (1 << 32),
+          v=BASE + (1 << 40) + (2 << 32), n=1000, chunks=BASE + (1 << 41), n_chunks=1, hp=None):
+    hp = zs.hparams(1) if hp is None else hp
+    return zs.raw_call("zero_shard_step_kahan", p, n_ranks, gdt, comp, m, v, n, chunks, n_chunks,
+                       ctypes.byref(hp), None)
+
+
+def test_kahan_step_argument_errors(zs):
+    E = zs
+    assert kahan(zs, None, 4) == E.ZERO_ERR_INVALID
+    assert kahan(zs, parts(4), 4, gdt=3) == E.ZERO_ERR_UNSUPPORTED
+    assert kahan(zs, parts(4), 4, comp=None) == E.ZERO_ERR_INVALID
+    assert kahan(zs, parts(4), 4, n=-1) == E.ZERO_ERR_INVALID
+    assert kahan(zs, parts(4), 4, chunks=None) == E.ZERO_ERR_INVALID
+    assert kahan(zs, parts(4), 4, hp=zs.hparams(0)) == E.ZERO_ERR_INVALID
+    assert kahan(zs, parts(4), 4, comp=BASE + (1 << 40) + 2) == E.ZERO_ERR_MISALIGNED
+    assert kahan(zs, parts(4), 4, v=BASE + (1 << 40) + (2 << 32) + 8) == E.ZERO_ERR_MISALIGNED
+    # comp over m (1000 bf16 = 2000 bytes), a partial over v
+    assert kahan(zs, parts(4), 4, m=BASE + (1 << 40) + 1024) == E.ZERO_ERR_ALIAS
+    assert kahan(zs, parts(4), 4, v=BASE + 16) == E.ZERO_ERR_ALIAS
+    # fake addresses that pass every other check launch nothing
+    assert kahan(zs, parts(4), 4) == E.ZERO_ERR_NOT_DEVICE
+    nulls = (ctypes.c_void_p * 4)(None, None, None, None)
+    assert kahan(zs, nulls, 4, comp=None, m=None, v=None, n=0, chunks=None, n_chunks=0) == E.ZERO_OK
 
 
 def test_non_device_addresses_are_rejected(zs):

@@ -13,7 +13,7 @@ import pytest
 import oracle
 import synth
 from synth import workloads as W
-from gpu_helpers import check_state, host_master, host_partials, oracle_warm_prefix, sample_indices, say
+from gpu_helpers import assert_bitwise, check_state, host_master, host_partials, oracle_warm_prefix, sample_indices, say
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -133,6 +133,69 @@ def test_llama70b_sampled_two_steps(bench):
     for t in (t0, t0 + 1):
         th, m, v, p = oracle.shard_step(parts, th, m, v, oracle.hparams(t, **w.hparams()))
     check_state(gather_state(sh, idx), (th, m, v, p), "70b sampled")
+    del sh
+    release()
+
+
+def gather_kahan(sh, idx):
+    i = torch.from_numpy(idx).to(sh.dev)
+    return (sh.param_at(idx), sh.comp[i].cpu().numpy().view(np.uint16),
+            sh.m[i].cpu().numpy().view(np.uint16), sh.v[i].cpu().numpy().view(np.uint16))
+
+
+def assert_kahan_state(got, want, what):
+    for name, g, w_ in zip(("parameters", "compensation", "m", "v"), got, want):
+        assert_bitwise(g, w_, f"{what} {name}")
+
+
+def test_gpt2_kahan_full_five_steps(bench):
+    """The pure-bf16 state in the bench's set-up (parameters written from the
+    initial fp32 master, zero compensation and moments), five steps, full
+    compare."""
+    w = W.gpt2()
+    say(f"case: {w.name} rank 2, pure-bf16 Kahan state, 5 steps, full compare")
+    sh = bench.Shard(w, rank=2)
+    sh.use_kahan()
+    idx = np.arange(sh.lo, sh.hi, dtype=np.int64)
+    th = oracle.bf16_round(host_master(w, idx))
+    c = np.zeros(sh.n, np.uint16)
+    m = np.zeros(sh.n, np.uint16)
+    v = np.zeros(sh.n, np.uint16)
+    for t in range(1, 6):
+        sh.fill_partials(t)
+        sh.step_kahan(t)
+        th, c, m, v = oracle.shard_step_kahan(host_partials(w, t, idx), th, c, m, v,
+                                              oracle.hparams(t, **w.hparams()))
+    flat = np.concatenate([host(x) for x in sh.params])
+    assert_kahan_state((flat[sh.lo:sh.hi], host(sh.comp), host(sh.m), host(sh.v)), (th, c, m, v),
+                       "gpt2 Kahan step 5")
+    del sh
+    release()
+
+
+def test_llama7b_kahan_sampled(bench):
+    """bench.py --state bf16-kahan on the 7B shard: warm start, switch to the
+    pure-bf16 state, three steps; sampled compare."""
+    w = W.llama7b()
+    say(f"case: {w.name} rank 0, warm start then pure-bf16 Kahan state, 3 steps, sampled")
+    sh = bench.Shard(w, rank=0)
+    t0 = sh.prepare()
+    sh.use_kahan()
+    steps = [t0, t0 + 1, t0 + 2]
+    for t in steps:
+        sh.step_kahan(t)
+    P = w.warm_prefix
+    pth, pm, pv = oracle_warm_prefix(w, sh.lo)
+    idx = sample_indices(sh.table, sh.n, seed=17)
+    say(f"  {idx.size} sampled indices")
+    src = synth.prefix_src(w.seed, synth.stream_id(synth.KIND_PREFIX_MAP), idx, P)
+    th32 = np.where(idx < P, pth[np.minimum(idx, P - 1)], host_master(w, sh.lo + idx)).astype(np.float32)
+    th, m, v = oracle.bf16_round(th32), oracle.bf16_round(pm[src]), oracle.bf16_round(pv[src])
+    c = np.zeros(idx.size, np.uint16)
+    parts = host_partials(w, t0, sh.lo + idx)     # the bench reuses step t0's partials
+    for t in steps:
+        th, c, m, v = oracle.shard_step_kahan(parts, th, c, m, v, oracle.hparams(t, **w.hparams()))
+    assert_kahan_state(gather_kahan(sh, idx), (th, c, m, v), "7b Kahan sampled")
     del sh
     release()
 
