@@ -91,3 +91,18 @@ def test_trace_summary_groups_by_kernel_and_grid(tmp_path):
     assert lines[2].startswith("| k_a | 64 | 64 | 2 | 2.0 | 2.0 | 1.0 | 3.0 |")
     assert lines[3].startswith("| k_a | 128 | 64 | 1 | 0.5 |")
     assert lines[4].startswith("| k_b | 256 | 256 | 1 | 0.1 |")
+
+
+@pytest.mark.parametrize("n_ranks,gdt", [(8, "bf16"), (16, "bf16"), (32, "f32")])
+def test_bench_byte_model_matches_the_ledger(n_ranks, gdt):
+    """The algorithmic bytes bench.py prices each state layout at are the
+    oracle ledger's per-element step bytes (2N + 26, 2N + 18, 2N + 16 with
+    bf16 partials)."""
+    from oracle import ledger
+    gb = 2 if gdt == "bf16" else 4
+    want = {"fp32": ledger.shard_step_bytes_per_param(n_ranks, gb, 4),
+            "bf16-moments": ledger.shard_step_bytes_per_param(n_ranks, gb, 2),
+            "bf16-kahan": ledger.kahan_step_bytes_per_param(n_ranks, gb)}
+    assert set(want) == set(bench.STATES)
+    for state, (_, rd, wr, _) in bench.STATES.items():
+        assert n_ranks * gb + rd + wr == want[state], state
