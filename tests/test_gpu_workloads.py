@@ -200,6 +200,61 @@ def test_llama7b_kahan_sampled(bench):
     release()
 
 
+def test_llama7b_bf16_moments_sampled(bench):
+    """bench.py --state bf16-moments on the 7B shard: warm start, moments
+    rounded to bf16, three steps; sampled compare."""
+    w = W.llama7b()
+    say(f"case: {w.name} rank 0, warm start then 12-byte state, 3 steps, sampled")
+    sh = bench.Shard(w, rank=0)
+    t0 = sh.prepare()
+    sh.use_bf16_moments()
+    steps = [t0, t0 + 1, t0 + 2]
+    for t in steps:
+        sh.step_bf16_moments(t)
+    P = w.warm_prefix
+    pth, pm, pv = oracle_warm_prefix(w, sh.lo)
+    idx = sample_indices(sh.table, sh.n, seed=27)
+    say(f"  {idx.size} sampled indices")
+    src = synth.prefix_src(w.seed, synth.stream_id(synth.KIND_PREFIX_MAP), idx, P)
+    th = np.where(idx < P, pth[np.minimum(idx, P - 1)], host_master(w, sh.lo + idx)).astype(np.float32)
+    m, v = oracle.bf16_round(pm[src]), oracle.bf16_round(pv[src])
+    parts = host_partials(w, t0, sh.lo + idx)
+    for t in steps:
+        th, m, v, p = oracle.shard_step_bf16m(parts, th, m, v, oracle.hparams(t, **w.hparams()))
+    i = torch.from_numpy(idx).to(sh.dev)
+    assert_bitwise(sh.master[i].cpu().numpy(), th, "7b 12-byte master")
+    assert_bitwise(sh.m[i].cpu().numpy().view(np.uint16), m, "7b 12-byte m")
+    assert_bitwise(sh.v[i].cpu().numpy().view(np.uint16), v, "7b 12-byte v")
+    assert_bitwise(sh.param_at(idx), p, "7b 12-byte parameters")
+    del sh
+    release()
+
+
+def test_llama70b_kahan_sampled(bench):
+    """bench.py --workload llama70b --state bf16-kahan: rank 5's slot (shard
+    elements past 2^32), two steps; sampled compare."""
+    w = W.llama70b()
+    say(f"case: {w.name} rank 5 slot, pure-bf16 Kahan state, 2 steps, sampled")
+    sh = bench.Shard(w, rank=5)
+    assert sh.n > (1 << 32)
+    t0 = sh.prepare()
+    sh.use_kahan()
+    sh.step_kahan(t0)
+    sh.step_kahan(t0 + 1)
+    idx = sample_indices(sh.table, sh.n, seed=75)
+    idx = np.unique(np.concatenate([idx, np.array([(1 << 32) - 1, 1 << 32, (1 << 32) + 7])]))
+    say(f"  {idx.size} sampled indices")
+    th = oracle.bf16_round(host_master(w, sh.lo + idx))
+    z = np.zeros(idx.size, np.uint16)
+    c, m, v = z.copy(), z.copy(), z.copy()
+    parts = host_partials(w, t0, sh.lo + idx)
+    for t in (t0, t0 + 1):
+        th, c, m, v = oracle.shard_step_kahan(parts, th, c, m, v, oracle.hparams(t, **w.hparams()))
+    assert_kahan_state(gather_kahan(sh, idx), (th, c, m, v), "70b Kahan sampled")
+    del sh
+    release()
+
+
 @pytest.mark.parametrize("bucket_params", [1 << 20, 3_000_000])
 def test_gpt2_bucketed_step_equals_oracle(bench, bucket_params):
     """ZeRO-2 bucketed step: one launch per bucket (a contiguous run of the
