@@ -51,10 +51,35 @@ STATES = {
 }
 
 
-def kernel_source_hash() -> str:
+def code_text(src: str) -> str:
+    """C/C++/HIP source with comments removed and whitespace collapsed: what
+    the compiler sees, so that editing a comment keeps recorded counters."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        if src.startswith("//", i):
+            i = src.find("\n", i)
+            i = n if i < 0 else i
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif src[i] in "\"'":
+            q, j = src[i], i + 1
+            while j < n and src[j] != q:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(src[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def kernel_source_hash(sources=None) -> str:
+    """Hash of the code (not the comments) of the kernel and host sources."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        h.update(open(p, "rb").read())
+    for p in sources or KERNEL_SOURCES:
+        h.update(code_text(open(p).read()).encode())
     return h.hexdigest()[:16]
 
 

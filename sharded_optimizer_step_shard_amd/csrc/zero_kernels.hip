@@ -494,13 +494,6 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
     }
 }
 
-// A workgroup (one wave) takes chunks blockIdx.x, blockIdx.x + gridDim.x,
-// ...: the grid is capped so that work-items stay below 2^32 however long
-// the table is.  At most one wave per SIMD (waves_per_eu): with fewer
-// concurrent streams the HBM sustains more of its peak on this mixed
-// read/write stream, measured across chunk sizes and block shapes on
-// MI355X (4 resident waves per CU beat 8-16).  Each wave still keeps its
-// group's 14 (N = 8) to 22 (N = 16) 16-byte loads in flight at once.
 // The step on the 12-byte state: fp32 master, bf16 m and v (in a.m, a.v
 // as 16-bit patterns).  Same reduce and AdamW; the moments are read from
 // bf16 and rounded back to bf16 once, from double.
@@ -641,6 +634,17 @@ void shard_step_m16_kernel(StepArgs a)
         step_chunk_m16<G, NC>(a, chunk_at(a.chunks, ci));
 }
 
+// In every chunk-table kernel a workgroup (one wave) takes chunks
+// blockIdx.x, blockIdx.x + gridDim.x, ...: the grid is capped so that
+// work-items stay below 2^32 however long the table is.
+//
+// The 16-byte step keeps at most one wave per SIMD (waves_per_eu): with
+// fewer concurrent streams the HBM sustains more of its peak on this mixed
+// read/write stream.  Measured on MI355X across chunk sizes and block
+// shapes, 4 resident waves per CU beat 8-16 (7B shard: 0.71 against 0.63-0.64
+// with two to four waves per SIMD).  Each wave still keeps its group's 14
+// (N = 8) to 22 (N = 16) 16-byte loads in flight at once.
+//
 // KC (extended step only): -1 flat rank order, 0 two-level with the group
 // size at run time, > 0 two-level with that group size.
 template <zero_dtype G, int NC, bool EXT, int KC = -1>

@@ -106,3 +106,13 @@ def test_bench_byte_model_matches_the_ledger(n_ranks, gdt):
     assert set(want) == set(bench.STATES)
     for state, (_, rd, wr, _) in bench.STATES.items():
         assert n_ranks * gb + rd + wr == want[state], state
+
+
+def test_code_hash_ignores_comments_not_code():
+    a = 'int f(int x) { return x + 1; } // one\n/* two */ const char *s = "a // b";\n'
+    b = 'int f(int x)\n{\n    return x + 1;   /* changed comment */\n}\nconst char *s = "a // b";\n'
+    c = 'int f(int x) { return x + 2; }\nconst char *s = "a // b";\n'
+    d = 'int f(int x) { return x + 1; }\nconst char *s = "a / b";\n'
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
+    assert bench.code_text(a) != bench.code_text(d)
