@@ -22,7 +22,10 @@
  *
  * zero_shard_step does all three in one pass over HBM; zero_reduce_shard,
  * zero_adamw_shard and zero_gather_write do them one at a time and give the
- * same bits.
+ * same bits.  Variants of the fused pass: zero_shard_step_ex (two-level
+ * reduce order, gradient accumulation), zero_shard_step_bf16_moments (fp32
+ * master with bf16 m, v) and zero_shard_step_kahan (pure bf16 state with a
+ * compensated update, no fp32 master).
  *
  * Arithmetic, fixed so that every result is reproducible bit for bit:
  *   - g: the partials are widened exactly to double and summed in double,
@@ -54,7 +57,12 @@
  *     (ALIAS), and finally that every array range lies inside one device
  *     allocation (NOT_DEVICE, via hipMemGetAddressRange).  The chunk
  *     table's dst addresses live in device memory and are not checked: they
- *     must come from zero_build_chunks over live parameter buffers.
+ *     must come from zero_build_chunks over live parameter buffers, and a
+ *     table names each shard element at most once (tables from
+ *     zero_build_chunks, and contiguous runs of their chunks, do).
+ *   - `gdt` arguments are plain ints holding a zero_dtype value; any other
+ *     value is UNSUPPORTED (the library converts to the enum only after the
+ *     check).
  *   - Base pointers of partials, state arrays and grad arrays must be 16-byte
  *     aligned (torch allocations are).  Lengths and offsets are arbitrary.
  *   - When the element count is 0 the call does nothing and its array
@@ -73,7 +81,7 @@ extern "C" {
 /* Element type of the gradient partials. */
 typedef enum zero_dtype {
     ZERO_BF16 = 0,   /* bfloat16, passed as 16-bit patterns */
-    ZERO_FP32 = 1    /* IEEE binary32 (the pages' fp32-gradient communication case) */
+    ZERO_FP32 = 1    /* IEEE binary32 (gradients communicated in fp32) */
 } zero_dtype;
 
 /* AdamW hyper-parameters, in double.  `step` is t >= 1, the number of this
@@ -159,7 +167,7 @@ int zero_build_chunks(const int64_t *numels, int n_tensors, int n_ranks, int ran
  * bad hp), MISALIGNED, UNSUPPORTED (gdt), NOT_DEVICE, ALIAS (a partial overlaps master,
  * m or v, or those overlap each other), HIP.
  */
-int zero_shard_step(const void *const *partials, int n_ranks, zero_dtype gdt,
+int zero_shard_step(const void *const *partials, int n_ranks, int gdt,
                     float *master, float *m, float *v, int64_t shard_len,
                     const zero_chunk *d_chunks, int64_t n_chunks,
                     const zero_adamw_hparams *hp, hipStream_t stream);
@@ -197,7 +205,7 @@ typedef struct zero_reduce_spec {
  * does not divide n_ranks, micro_batches < 1, or acc is given iff
  * micro_batches == 1; ALIAS when acc overlaps master, m or v.
  */
-int zero_shard_step_ex(const void *const *partials, int n_ranks, zero_dtype gdt,
+int zero_shard_step_ex(const void *const *partials, int n_ranks, int gdt,
                        const zero_reduce_spec *rs, float *master, float *m, float *v,
                        int64_t shard_len, const zero_chunk *d_chunks, int64_t n_chunks,
                        const zero_adamw_hparams *hp, hipStream_t stream);
@@ -208,7 +216,7 @@ int zero_shard_step_ex(const void *const *partials, int n_ranks, zero_dtype gdt,
  * i in [0, n); with reset the sum alone is rounded (a -0 sum stays -0).
  * group as in zero_reduce_spec.  acc must not overlap a partial (ALIAS).
  */
-int zero_accumulate_shard(const void *const *partials, int n_ranks, zero_dtype gdt, int group,
+int zero_accumulate_shard(const void *const *partials, int n_ranks, int gdt, int group,
                           int64_t n, float *acc, int reset, hipStream_t stream);
 
 /*
@@ -221,7 +229,7 @@ int zero_accumulate_shard(const void *const *partials, int n_ranks, zero_dtype g
  * bytes per element (bf16 partials) instead of 2N + 26.  Errors as
  * zero_shard_step.
  */
-int zero_shard_step_bf16_moments(const void *const *partials, int n_ranks, zero_dtype gdt,
+int zero_shard_step_bf16_moments(const void *const *partials, int n_ranks, int gdt,
                                  float *master, uint16_t *m, uint16_t *v, int64_t shard_len,
                                  const zero_chunk *d_chunks, int64_t n_chunks,
                                  const zero_adamw_hparams *hp, hipStream_t stream);
@@ -243,7 +251,7 @@ int zero_shard_step_bf16_moments(const void *const *partials, int n_ranks, zero_
  * each shard element at most once (zero_build_chunks' tables do).  Errors
  * as zero_shard_step_bf16_moments, with comp in place of master.
  */
-int zero_shard_step_kahan(const void *const *partials, int n_ranks, zero_dtype gdt,
+int zero_shard_step_kahan(const void *const *partials, int n_ranks, int gdt,
                           uint16_t *comp, uint16_t *m, uint16_t *v, int64_t shard_len,
                           const zero_chunk *d_chunks, int64_t n_chunks,
                           const zero_adamw_hparams *hp, hipStream_t stream);
@@ -253,7 +261,7 @@ int zero_shard_step_kahan(const void *const *partials, int n_ranks, zero_dtype g
  * i in [0, n), summed in double in rank order.  grad_out must not overlap
  * any partial (ALIAS).  n == 0 is a no-op.
  */
-int zero_reduce_shard(const void *const *partials, int n_ranks, zero_dtype gdt, int64_t n,
+int zero_reduce_shard(const void *const *partials, int n_ranks, int gdt, int64_t n,
                       float *grad_out, hipStream_t stream);
 
 /*

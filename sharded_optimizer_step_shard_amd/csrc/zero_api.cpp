@@ -81,27 +81,36 @@ bool valid_reduce_spec(const zero_reduce_spec *rs, int n_ranks)
     return (rs->micro_batches > 1) == (rs->acc != nullptr);
 }
 
-int elem_bytes(zero_dtype gdt) { return gdt == ZERO_BF16 ? 2 : 4; }
+int elem_bytes(int gdt) { return gdt == ZERO_BF16 ? 2 : 4; }   // after valid_dtype
 
-// Shared checks of the partial list; fills pp.  With n == 0 nothing is
-// dereferenced, so null partial addresses are accepted (empty tensors).
-int check_partials(const void *const *partials, int n_ranks, zero_dtype gdt, int64_t n,
-                   PartialPtrs &pp)
+// The INVALID checks of the partial list (null list, rank count, null
+// partial); fills pp.  With n == 0 nothing is dereferenced, so null partial
+// addresses are accepted (empty tensors).  Alignment and dtype are checked
+// by the callers after all INVALID checks, in the order the header states.
+int check_partials(const void *const *partials, int n_ranks, int64_t n, PartialPtrs &pp)
 {
-    if (gdt != ZERO_BF16 && gdt != ZERO_FP32)
-        return ZERO_ERR_UNSUPPORTED;
     if (!partials || n_ranks < 1 || n_ranks > ZERO_MAX_RANKS)
         return ZERO_ERR_INVALID;
     memset(&pp, 0, sizeof(pp));
     for (int k = 0; k < n_ranks; ++k) {
         if (!partials[k] && n > 0)
             return ZERO_ERR_INVALID;
-        if (!aligned16(partials[k]))
-            return ZERO_ERR_MISALIGNED;
         pp.p[k] = partials[k];
     }
     return ZERO_OK;
 }
+
+bool partials_aligned(const PartialPtrs &pp, int n_ranks)
+{
+    for (int k = 0; k < n_ranks; ++k)
+        if (!aligned16(pp.p[k]))
+            return false;
+    return true;
+}
+
+// The dtype arrives as a plain int from C callers; only these values are
+// converted to zero_dtype.
+bool valid_dtype(int gdt) { return gdt == ZERO_BF16 || gdt == ZERO_FP32; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ZERO_OK : ZERO_ERR_HIP; }
 
@@ -216,21 +225,24 @@ int zero_build_chunks(const int64_t *numels, int n_tensors, int n_ranks, int ran
     return ZERO_OK;
 }
 
-int zero_shard_step(const void *const *partials, int n_ranks, zero_dtype gdt,
+int zero_shard_step(const void *const *partials, int n_ranks, int gdt,
                     float *master, float *m, float *v, int64_t shard_len,
                     const zero_chunk *d_chunks, int64_t n_chunks,
                     const zero_adamw_hparams *hp, hipStream_t stream)
 {
     StepArgs a{};
-    int rc = check_partials(partials, n_ranks, gdt, shard_len, a.parts);
+    int rc = check_partials(partials, n_ranks, shard_len, a.parts);
     if (rc)
         return rc;
     if (((!master || !m || !v) && shard_len > 0) || shard_len < 0 || n_chunks < 0 ||
         n_chunks > INT32_MAX ||
         (n_chunks > 0 && !d_chunks) || !valid_hparams(hp))
         return ZERO_ERR_INVALID;
-    if (!aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(d_chunks))
+    if (!partials_aligned(a.parts, n_ranks) || !aligned16(master) || !aligned16(m) ||
+        !aligned16(v) || !aligned16(d_chunks))
         return ZERO_ERR_MISALIGNED;
+    if (!valid_dtype(gdt))
+        return ZERO_ERR_UNSUPPORTED;
     const int64_t sb = shard_len * 4, gb = shard_len * elem_bytes(gdt);
     if (overlaps(master, sb, m, sb) || overlaps(master, sb, v, sb) || overlaps(m, sb, v, sb))
         return ZERO_ERR_ALIAS;
@@ -254,25 +266,27 @@ int zero_shard_step(const void *const *partials, int n_ranks, zero_dtype gdt,
     a.chunks = d_chunks;
     a.n_chunks = n_chunks;
     a.shard_len = shard_len;
-    return hip_status(launch_step(a, gdt, stream));
+    return hip_status(launch_step(a, (zero_dtype)gdt, stream));
 }
 
-int zero_shard_step_ex(const void *const *partials, int n_ranks, zero_dtype gdt,
+int zero_shard_step_ex(const void *const *partials, int n_ranks, int gdt,
                        const zero_reduce_spec *rs, float *master, float *m, float *v,
                        int64_t shard_len, const zero_chunk *d_chunks, int64_t n_chunks,
                        const zero_adamw_hparams *hp, hipStream_t stream)
 {
     StepArgs a{};
-    int rc = check_partials(partials, n_ranks, gdt, shard_len, a.parts);
+    int rc = check_partials(partials, n_ranks, shard_len, a.parts);
     if (rc)
         return rc;
     if (((!master || !m || !v) && shard_len > 0) || shard_len < 0 || n_chunks < 0 ||
         n_chunks > INT32_MAX || (n_chunks > 0 && !d_chunks) || !valid_hparams(hp) ||
         !valid_reduce_spec(rs, n_ranks))
         return ZERO_ERR_INVALID;
-    if (!aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(d_chunks) ||
-        !aligned16(rs->acc))
+    if (!partials_aligned(a.parts, n_ranks) || !aligned16(master) || !aligned16(m) ||
+        !aligned16(v) || !aligned16(d_chunks) || !aligned16(rs->acc))
         return ZERO_ERR_MISALIGNED;
+    if (!valid_dtype(gdt))
+        return ZERO_ERR_UNSUPPORTED;
     const int64_t sb = shard_len * 4, gb = shard_len * elem_bytes(gdt);
     if (overlaps(master, sb, m, sb) || overlaps(master, sb, v, sb) || overlaps(m, sb, v, sb))
         return ZERO_ERR_ALIAS;
@@ -301,23 +315,26 @@ int zero_shard_step_ex(const void *const *partials, int n_ranks, zero_dtype gdt,
     a.n_chunks = n_chunks;
     a.shard_len = shard_len;
     a.acc = rs->acc;
-    return hip_status(launch_step_ex(a, gdt, stream));
+    return hip_status(launch_step_ex(a, (zero_dtype)gdt, stream));
 }
 
-int zero_shard_step_bf16_moments(const void *const *partials, int n_ranks, zero_dtype gdt,
+int zero_shard_step_bf16_moments(const void *const *partials, int n_ranks, int gdt,
                                  float *master, uint16_t *m, uint16_t *v, int64_t shard_len,
                                  const zero_chunk *d_chunks, int64_t n_chunks,
                                  const zero_adamw_hparams *hp, hipStream_t stream)
 {
     StepArgs a{};
-    int rc = check_partials(partials, n_ranks, gdt, shard_len, a.parts);
+    int rc = check_partials(partials, n_ranks, shard_len, a.parts);
     if (rc)
         return rc;
     if (((!master || !m || !v) && shard_len > 0) || shard_len < 0 || n_chunks < 0 ||
         n_chunks > INT32_MAX || (n_chunks > 0 && !d_chunks) || !valid_hparams(hp))
         return ZERO_ERR_INVALID;
-    if (!aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(d_chunks))
+    if (!partials_aligned(a.parts, n_ranks) || !aligned16(master) || !aligned16(m) ||
+        !aligned16(v) || !aligned16(d_chunks))
         return ZERO_ERR_MISALIGNED;
+    if (!valid_dtype(gdt))
+        return ZERO_ERR_UNSUPPORTED;
     const int64_t fb = shard_len * 4, hb = shard_len * 2, gb = shard_len * elem_bytes(gdt);
     if (overlaps(master, fb, m, hb) || overlaps(master, fb, v, hb) || overlaps(m, hb, v, hb))
         return ZERO_ERR_ALIAS;
@@ -343,23 +360,26 @@ int zero_shard_step_bf16_moments(const void *const *partials, int n_ranks, zero_
     a.shard_len = shard_len;
     a.acc = nullptr;
     a.comp = nullptr;
-    return hip_status(launch_step_m16(a, gdt, stream));
+    return hip_status(launch_step_m16(a, (zero_dtype)gdt, stream));
 }
 
-int zero_shard_step_kahan(const void *const *partials, int n_ranks, zero_dtype gdt,
+int zero_shard_step_kahan(const void *const *partials, int n_ranks, int gdt,
                           uint16_t *comp, uint16_t *m, uint16_t *v, int64_t shard_len,
                           const zero_chunk *d_chunks, int64_t n_chunks,
                           const zero_adamw_hparams *hp, hipStream_t stream)
 {
     StepArgs a{};
-    int rc = check_partials(partials, n_ranks, gdt, shard_len, a.parts);
+    int rc = check_partials(partials, n_ranks, shard_len, a.parts);
     if (rc)
         return rc;
     if (((!comp || !m || !v) && shard_len > 0) || shard_len < 0 || n_chunks < 0 ||
         n_chunks > INT32_MAX || (n_chunks > 0 && !d_chunks) || !valid_hparams(hp))
         return ZERO_ERR_INVALID;
-    if (!aligned16(comp) || !aligned16(m) || !aligned16(v) || !aligned16(d_chunks))
+    if (!partials_aligned(a.parts, n_ranks) || !aligned16(comp) || !aligned16(m) ||
+        !aligned16(v) || !aligned16(d_chunks))
         return ZERO_ERR_MISALIGNED;
+    if (!valid_dtype(gdt))
+        return ZERO_ERR_UNSUPPORTED;
     const int64_t hb = shard_len * 2, gb = shard_len * elem_bytes(gdt);
     if (overlaps(comp, hb, m, hb) || overlaps(comp, hb, v, hb) || overlaps(m, hb, v, hb))
         return ZERO_ERR_ALIAS;
@@ -385,21 +405,23 @@ int zero_shard_step_kahan(const void *const *partials, int n_ranks, zero_dtype g
     a.n_chunks = n_chunks;
     a.shard_len = shard_len;
     a.acc = nullptr;
-    return hip_status(launch_step_kahan(a, gdt, stream));
+    return hip_status(launch_step_kahan(a, (zero_dtype)gdt, stream));
 }
 
-int zero_accumulate_shard(const void *const *partials, int n_ranks, zero_dtype gdt, int group,
+int zero_accumulate_shard(const void *const *partials, int n_ranks, int gdt, int group,
                           int64_t n, float *acc, int reset, hipStream_t stream)
 {
     AccArgs a;
-    int rc = check_partials(partials, n_ranks, gdt, n, a.parts);
+    int rc = check_partials(partials, n_ranks, n, a.parts);
     if (rc)
         return rc;
     if ((!acc && n > 0) || n < 0 || group < 0 || group > n_ranks ||
         (group > 0 && n_ranks % group != 0))
         return ZERO_ERR_INVALID;
-    if (!aligned16(acc))
+    if (!partials_aligned(a.parts, n_ranks) || !aligned16(acc))
         return ZERO_ERR_MISALIGNED;
+    if (!valid_dtype(gdt))
+        return ZERO_ERR_UNSUPPORTED;
     for (int k = 0; k < n_ranks; ++k)
         if (overlaps(partials[k], n * elem_bytes(gdt), acc, n * 4))
             return ZERO_ERR_ALIAS;
@@ -414,20 +436,22 @@ int zero_accumulate_shard(const void *const *partials, int n_ranks, zero_dtype g
     a.acc = acc;
     a.n = n;
     a.reset = reset ? 1 : 0;
-    return hip_status(launch_accumulate(a, gdt, stream));
+    return hip_status(launch_accumulate(a, (zero_dtype)gdt, stream));
 }
 
-int zero_reduce_shard(const void *const *partials, int n_ranks, zero_dtype gdt, int64_t n,
+int zero_reduce_shard(const void *const *partials, int n_ranks, int gdt, int64_t n,
                       float *grad_out, hipStream_t stream)
 {
     ReduceArgs a;
-    int rc = check_partials(partials, n_ranks, gdt, n, a.parts);
+    int rc = check_partials(partials, n_ranks, n, a.parts);
     if (rc)
         return rc;
     if ((!grad_out && n > 0) || n < 0)
         return ZERO_ERR_INVALID;
-    if (!aligned16(grad_out))
+    if (!partials_aligned(a.parts, n_ranks) || !aligned16(grad_out))
         return ZERO_ERR_MISALIGNED;
+    if (!valid_dtype(gdt))
+        return ZERO_ERR_UNSUPPORTED;
     for (int k = 0; k < n_ranks; ++k)
         if (overlaps(partials[k], n * elem_bytes(gdt), grad_out, n * 4))
             return ZERO_ERR_ALIAS;
@@ -441,7 +465,7 @@ int zero_reduce_shard(const void *const *partials, int n_ranks, zero_dtype gdt, 
     a.red = make_reduce(n_ranks);
     a.out = grad_out;
     a.n = n;
-    return hip_status(launch_reduce(a, gdt, stream));
+    return hip_status(launch_reduce(a, (zero_dtype)gdt, stream));
 }
 
 int zero_adamw_shard(const float *grad, float *master, float *m, float *v, int64_t n,

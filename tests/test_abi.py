@@ -284,3 +284,28 @@ def test_extended_reduce_argument_errors(zs):
     assert acc_call(parts(4), 4, 0, 2, 100, BASE + 64, 1, None) == zs.ZERO_ERR_ALIAS
     assert acc_call(parts(4), 4, 0, 2, 100, acc, 0, None) == zs.ZERO_ERR_NOT_DEVICE
     assert acc_call((ctypes.c_void_p * 4)(), 4, 0, 2, 0, None, 1, None) == zs.ZERO_OK
+
+
+def test_checks_run_in_the_documented_order(zs):
+    """A call with several faults returns the first in the header's order:
+    INVALID, MISALIGNED, UNSUPPORTED, ALIAS, NOT_DEVICE.  A bad dtype is an
+    int the library never converts to its enum (the ABI takes an int)."""
+    E = zs
+    p = parts(4)
+    mis = parts(4)
+    mis[1] = BASE + (1 << 30) + 8
+    # null master + misaligned partial + bad dtype -> INVALID
+    assert step(zs, mis, 4, gdt=9, master=None) == E.ZERO_ERR_INVALID
+    # misaligned partial + bad dtype + aliasing master -> MISALIGNED
+    assert step(zs, mis, 4, gdt=9, master=BASE) == E.ZERO_ERR_MISALIGNED
+    # bad dtype + aliasing master -> UNSUPPORTED
+    assert step(zs, p, 4, gdt=-1, master=BASE) == E.ZERO_ERR_UNSUPPORTED
+    assert step(zs, p, 4, gdt=1 << 30) == E.ZERO_ERR_UNSUPPORTED
+    # aliasing master + fake (non-device) addresses -> ALIAS
+    assert step(zs, p, 4, master=BASE) == E.ZERO_ERR_ALIAS
+    assert step(zs, p, 4) == E.ZERO_ERR_NOT_DEVICE
+    out = BASE + (1 << 40)
+    assert zs.raw_call("zero_reduce_shard", mis, 4, 9, 10, out, None) == E.ZERO_ERR_MISALIGNED
+    assert zs.raw_call("zero_reduce_shard", p, 4, 9, 10, out, None) == E.ZERO_ERR_UNSUPPORTED
+    assert zs.raw_call("zero_accumulate_shard", mis, 4, 9, 0, 10, out, 1, None) == E.ZERO_ERR_MISALIGNED
+    assert zs.raw_call("zero_accumulate_shard", p, 4, 9, 0, 10, out, 1, None) == E.ZERO_ERR_UNSUPPORTED

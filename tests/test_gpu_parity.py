@@ -385,3 +385,85 @@ def test_bf16_moment_rounding_at_midpoints(zs):
     assert_bitwise(host(m), want[1], "moments at midpoints: m")
     assert_bitwise(host(v), want[2], "moments at midpoints: v")
     assert_bitwise(host(master), want[0], "moments at midpoints: master")
+
+
+# ------------------------------------------------------------ checkpoint / resume
+
+@pytest.mark.parametrize("state", ["fp32", "bf16-kahan"])
+def test_checkpoint_resume_is_bitwise(zs, tmp_path, state):
+    """Kill-and-replay: three steps, the shard state (and t) saved to .npy
+    files, every device buffer freed, the state reloaded into new
+    allocations with a newly built chunk table, three more steps.  The
+    result equals the uninterrupted six-step run bit for bit, and both equal
+    the oracle."""
+    say(f"case: checkpoint/resume, {state} state")
+    w = W.Workload("ckpt", 97, [5_000, 70_001, 3], 4, "bf16", 1e-3)
+    rank = 1
+    lo, hi = w.shard_range(rank)
+    n = hi - lo
+    idx = np.arange(lo, hi, dtype=np.int64)
+    th0 = host_master(w, idx)
+
+    def fresh(arrays):
+        full = torch.full((sum(w.numels),), -1, dtype=torch.int16, device="cuda")
+        table, _ = zs.zero_build_chunks(w.numels, w.n_ranks, rank, slot_dst=full.data_ptr() + 2 * lo,
+                                        max_chunk=960)
+        if state == "fp32":
+            bufs = [dev(arrays[0]), dev(arrays[1]), dev(arrays[2])]
+        else:
+            full[lo:hi] = torch.from_numpy(arrays[0].view(np.int16)).cuda()
+            bufs = [dev_bf16(arrays[1]), dev_bf16(arrays[2]), dev_bf16(arrays[3])]
+        return full, bufs, zs.chunks_to_device(table), len(table)
+
+    def run(full, bufs, d_table, n_chunks, steps):
+        for t in steps:
+            parts = [dev_bf16(p) for p in host_partials(w, t, idx)]
+            if state == "fp32":
+                zs.zero_shard_step(parts, *bufs, n, d_table, n_chunks, zs.hparams(t, **HP))
+            else:
+                zs.zero_shard_step_kahan(parts, *bufs, n, d_table, n_chunks, zs.hparams(t, **HP))
+        torch.cuda.synchronize()
+
+    def snapshot(full, bufs):
+        p = host(full)[lo:hi].copy()
+        return [host(b).copy() for b in bufs] + [p] if state == "fp32" else [p] + [host(b).copy() for b in bufs]
+
+    z32, z16 = np.zeros(n, np.float32), np.zeros(n, np.uint16)
+    init = [th0, z32, z32] if state == "fp32" else [oracle.bf16_round(th0), z16, z16, z16]
+    # uninterrupted
+    full, bufs, d_table, nc = fresh(init)
+    run(full, bufs, d_table, nc, range(1, 7))
+    straight = snapshot(full, bufs)
+    del full, bufs, d_table
+    # interrupted after step 3, resumed from files
+    full, bufs, d_table, nc = fresh(init)
+    run(full, bufs, d_table, nc, range(1, 4))
+    saved = snapshot(full, bufs)
+    for k, a in enumerate(saved):
+        np.save(tmp_path / f"s{k}.npy", a)
+    np.save(tmp_path / "t.npy", np.array([3], np.int64))
+    del full, bufs, d_table
+    torch.cuda.empty_cache()
+    loaded = [np.load(tmp_path / f"s{k}.npy") for k in range(len(saved))]
+    t_done = int(np.load(tmp_path / "t.npy")[0])
+    arrays = loaded[:3] if state == "fp32" else loaded
+    full, bufs, d_table, nc = fresh(arrays)
+    if state == "fp32":
+        full[lo:hi] = torch.from_numpy(loaded[3].view(np.int16)).cuda()
+    run(full, bufs, d_table, nc, range(t_done + 1, 7))
+    resumed = snapshot(full, bufs)
+    for k, (a, b) in enumerate(zip(straight, resumed)):
+        assert_bitwise(b, a, f"resume {state} array {k}", strict_nan=True)
+    # and the oracle's six steps
+    if state == "fp32":
+        th, m, v = th0, z32, z32
+        for t in range(1, 7):
+            th, m, v, p = oracle.shard_step(host_partials(w, t, idx), th, m, v, oracle.hparams(t, **HP))
+        want = [th, m, v, p]
+    else:
+        th, c, m, v = init
+        for t in range(1, 7):
+            th, c, m, v = oracle.shard_step_kahan(host_partials(w, t, idx), th, c, m, v, oracle.hparams(t, **HP))
+        want = [th, c, m, v]
+    for k, (a, b) in enumerate(zip(want, straight)):
+        assert_bitwise(b, a, f"oracle {state} array {k}")
