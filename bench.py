@@ -408,6 +408,49 @@ def probe_read(nbytes: int, reps: int = 5) -> dict:
             "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def launch_overhead(n_ranks: int = 8, n: int = 1 << 16, calls: int = 4000) -> dict:
+    """Per-call cost of zero_shard_step on a small shard (n elements, 32
+    chunks): the C call through ctypes with no chunks (argument checks only),
+    the full C call (checks, one device-range query per array, launch; host
+    issue time and time including the GPU's completion), and the same through
+    the Python binding.  Microseconds per call."""
+    import ctypes
+    import torch
+    import sharded_optimizer_step_shard_amd as zs
+    parts = [torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(n_ranks)]
+    master, m, v = (torch.zeros(n, device="cuda") for _ in range(3))
+    slot = torch.zeros(n, dtype=torch.int16, device="cuda")
+    table, _ = zs.zero_build_chunks([n], 1, 0, slot_dst=slot)
+    d_table = zs.chunks_to_device(table)
+    hp = zs.hparams(3)
+    stream = torch.cuda.current_stream().cuda_stream
+    pp = (ctypes.c_void_p * n_ranks)(*[p.data_ptr() for p in parts])
+    full = (pp, n_ranks, 0, master.data_ptr(), m.data_ptr(), v.data_ptr(), n, d_table.data_ptr(),
+            len(table), ctypes.byref(hp), stream)
+    empty = full[:8] + (0,) + full[9:]
+    lib = zs.lib()
+
+    def per_call(fn):
+        for _ in range(200):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            fn()
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        return (t1 - t0) / calls * 1e6, (t2 - t0) / calls * 1e6
+
+    checks, _ = per_call(lambda: lib.zero_shard_step(*empty))
+    c_issue, c_done = per_call(lambda: lib.zero_shard_step(*full))
+    py_issue, py_done = per_call(lambda: zs.zero_shard_step(parts, master, m, v, n, d_table,
+                                                            len(table), hp))
+    return {"elements": n, "chunks": len(table), "n_ranks": n_ranks, "calls": calls,
+            "c_checks_only_us": checks, "c_full_issue_us": c_issue, "c_full_with_gpu_us": c_done,
+            "python_issue_us": py_issue, "python_with_gpu_us": py_done}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -556,12 +599,17 @@ def main() -> int:
                     help="no GPU: turn the counter_collection CSVs of two rocprofv3 passes "
                          "(--pmc FETCH_SIZE, --pmc WRITE_SIZE) over this same command into "
                          "calibrated HBM bytes per launch, recorded in profiles/traffic.json")
+    ap.add_argument("--launch-overhead", action="store_true",
+                    help="print the per-call cost of zero_shard_step on a small shard (JSON)")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="no GPU: print a markdown table of a rocprofv3 kernel trace")
     args = ap.parse_args()
 
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
+        return 0
+    if args.launch_overhead:
+        print(json.dumps(launch_overhead()), flush=True)
         return 0
     if args.ingest_counters:
         rec = ingest_counters(*args.ingest_counters, W.get(args.workload), args.rank, args.state,
