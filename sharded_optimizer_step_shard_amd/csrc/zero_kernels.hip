@@ -43,15 +43,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ double bf16_lo(uint32_t w) { return (double)__uint_as_float(w << 16); }
 __device__ __forceinline__ double bf16_hi(uint32_t w) { return (double)__uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16, round to nearest even.  Adding 0x7FFF plus the lowest kept
-// bit carries into the kept half exactly when the dropped half is above
-// one half, or equal to it with an odd kept half.  NaN: keep sign and top
-// payload, set the quiet bit.
+// fp32 -> bf16, round to nearest even; NaN keeps its sign and top payload
+// bits with the quiet bit set; overflow gives inf.  gfx950 converts in one
+// instruction (v_cvt_pk_bf16_f32).  On MI355X its result equals, for all
+// 2^32 fp32 patterns, the integer rounding (u + 0x7FFF + kept lsb) >> 16
+// with NaN mapped to (u >> 16) | 0x40, which is what the oracle computes.
 __device__ __forceinline__ uint32_t to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : r;
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // Sum -> fp32 mean.  With N a compile-time power of two the division is a
