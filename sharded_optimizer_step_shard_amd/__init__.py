@@ -61,7 +61,7 @@ class ZeroShardError(RuntimeError):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it first "
-                      "(python -m sharded_optimizer_step_shard_amd.build)")
+                      f"(python {os.path.join(_PKG, 'build.py')})")
 
 _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
