@@ -451,6 +451,36 @@ def launch_overhead(n_ranks: int = 8, n: int = 1 << 16, calls: int = 4000) -> di
             "python_issue_us": py_issue, "python_with_gpu_us": py_done}
 
 
+def probe_write(nbytes: int, reps: int = 5) -> dict:
+    """Write-only stream over nbytes with zero_probe_write (the step kernels'
+    non-temporal stores): the attainable write rate."""
+    import torch
+    import sharded_optimizer_step_shard_amd as zs
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    zs.zero_probe_write(dst, nbytes)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        zs.zero_probe_write(dst, nbytes)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del dst
+    torch.cuda.empty_cache()
+    return {"bytes_written": nbytes, "ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def mix_bound(read_bytes: float, write_bytes: float, read_gbs: float, write_gbs: float) -> float:
+    """Attainable GB/s of a stream that moves read_bytes and write_bytes if
+    the reads go at the read-only rate and the writes at the write-only rate,
+    one after the other: (R + W) / (R / r + W / w)."""
+    return (read_bytes + write_bytes) / (read_bytes / read_gbs + write_bytes / write_gbs)
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -732,9 +762,18 @@ def main() -> int:
     if args.probe_copy > 0:
         out["probe_copy"] = probe_copy(args.probe_copy)
         out["probe_read"] = probe_read(args.probe_copy)
+        out["probe_write"] = probe_write(args.probe_copy)
         # the step's rate against the rates this GPU sustained on plain streams
         out["roofline"]["vs_copy_probe"] = achieved / out["probe_copy"]["gbs"]
         out["roofline"]["vs_read_probe"] = achieved / out["probe_read"]["gbs"]
+        _, rd, wr, _ = STATES[args.state]
+        gb = 2 if w.gdt == "bf16" else 4
+        rb, wb = (w.n_ranks * gb + rd) * sh.n, wr * sh.n
+        if extended and args.micro_batches > 1:
+            rb += 4 * sh.n
+        bound = mix_bound(rb, wb, out["probe_read"]["gbs"], out["probe_write"]["gbs"])
+        out["roofline"]["mix_model"] = {"read_bytes": rb, "write_bytes": wb, "bound_gbs": bound,
+                                        "frac_of_bound": achieved / bound}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.rank, t, args.cpu_seconds, state=args.state)
     print(json.dumps(out), flush=True)

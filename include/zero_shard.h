@@ -304,6 +304,15 @@ int zero_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t strea
 int zero_probe_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t magic,
                     hipStream_t stream);
 
+/*
+ * Measurement aid, not part of the step: writes `value` to every 32-bit word
+ * of dst (device, 16-byte aligned; a trailing partial word gets its low
+ * bytes) with the step kernels' non-temporal 16-byte stores.  Gives the
+ * attainable write-only HBM rate beside the read and copy rates.
+ * Errors: INVALID (null with bytes > 0, bytes < 0), MISALIGNED, NOT_DEVICE.
+ */
+int zero_probe_write(void *dst, int64_t bytes, uint32_t value, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -81,10 +81,12 @@ _lib.zero_adamw_shard.argtypes = [_vp, _vp, _vp, _vp, _i64, ctypes.POINTER(HPara
 _lib.zero_gather_write.argtypes = [_vp, _i64, _vp, _i64, _vp]
 _lib.zero_probe_copy.argtypes = [_vp, _vp, _i64, _vp]
 _lib.zero_probe_read.argtypes = [_vp, _i64, _vp, ctypes.c_uint32, _vp]
+_lib.zero_probe_write.argtypes = [_vp, _i64, ctypes.c_uint32, _vp]
 _lib.zero_strerror.argtypes = [_i32]
 _lib.zero_strerror.restype = ctypes.c_char_p
 for _f in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
-           "zero_gather_write", "zero_probe_copy", "zero_probe_read", "zero_version", "zero_shard_step_ex",
+           "zero_gather_write", "zero_probe_copy", "zero_probe_read", "zero_probe_write",
+           "zero_version", "zero_shard_step_ex",
            "zero_accumulate_shard", "zero_shard_step_bf16_moments", "zero_shard_step_kahan"):
     getattr(_lib, _f).restype = _i32
 
@@ -260,6 +262,10 @@ def zero_probe_copy(src: Ptr, dst: Ptr, nbytes: int, stream=None) -> None:
 def zero_probe_read(src: Ptr, nbytes: int, sink: Ptr, magic: int = 0x9E3779B9, stream=None) -> None:
     _check(_lib.zero_probe_read(_addr(src), nbytes, _addr(sink), magic, _stream(stream)),
            "zero_probe_read")
+
+
+def zero_probe_write(dst: Ptr, nbytes: int, value: int = 0x3C003C00, stream=None) -> None:
+    _check(_lib.zero_probe_write(_addr(dst), nbytes, value, _stream(stream)), "zero_probe_write")
 
 
 def raw_call(name: str, *args) -> int:

@@ -134,7 +134,7 @@ bool in_device_alloc(const void *p, int64_t bytes)
 
 extern "C" {
 
-int zero_version(void) { return (1 << 16) | 4; }
+int zero_version(void) { return (1 << 16) | 5; }
 
 const char *zero_strerror(int code)
 {
@@ -541,6 +541,19 @@ int zero_probe_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t mag
     if (!in_device_alloc(src, bytes) || !in_device_alloc(sink, 4))
         return ZERO_ERR_NOT_DEVICE;
     return hip_status(launch_probe_read(src, bytes, sink, magic, stream));
+}
+
+int zero_probe_write(void *dst, int64_t bytes, uint32_t value, hipStream_t stream)
+{
+    if ((!dst && bytes > 0) || bytes < 0)
+        return ZERO_ERR_INVALID;
+    if (!aligned16(dst))
+        return ZERO_ERR_MISALIGNED;
+    if (bytes == 0)
+        return ZERO_OK;
+    if (!in_device_alloc(dst, bytes))
+        return ZERO_ERR_NOT_DEVICE;
+    return hip_status(launch_probe_write(dst, bytes, value, stream));
 }
 
 }  // extern "C"

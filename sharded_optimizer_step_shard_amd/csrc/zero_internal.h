@@ -88,5 +88,6 @@ hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s);
 hipError_t launch_probe_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t magic,
                              hipStream_t s);
+hipError_t launch_probe_write(void *dst, int64_t bytes, uint32_t value, hipStream_t s);
 
 }  // namespace zs

@@ -827,6 +827,27 @@ __global__ __launch_bounds__(kBlock) void probe_read_kernel(const u32x4 *src, in
         sink[0] = x;
 }
 
+// Write-only stream: workgroup b writes 4 KiB pieces b, b + gridDim.x, ...
+// with one non-temporal 16-byte store per lane (the store the step kernels
+// use for their state), the bytes past the last full word element by
+// element.  The value written is `value` in every 32-bit word.
+__global__ __launch_bounds__(kBlock) void probe_write_kernel(u32x4 *dst, int64_t n16,
+                                                             uint8_t *dst_b, int64_t bytes,
+                                                             uint32_t value)
+{
+    const u32x4 w = {value, value, value, value};
+    for (int64_t p = blockIdx.x; p * kReadPiece < n16; p += gridDim.x) {
+        const int64_t i = p * kReadPiece + threadIdx.x;
+        if (i < n16)
+            st_nt(dst + i, w);
+    }
+    if (blockIdx.x == 0) {
+        const int64_t b = n16 * 16 + threadIdx.x;
+        if (b < bytes)
+            dst_b[b] = (uint8_t)value;
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 
 static int grid_for(int64_t items)
@@ -1054,6 +1075,19 @@ hipError_t launch_probe_read(const void *src, int64_t bytes, uint32_t *sink, uin
         pieces = 1;
     hipLaunchKernelGGL(probe_read_kernel, dim3((int)pieces), dim3(kBlock), 0, s, (const u32x4 *)src,
                        n16, (const uint8_t *)src, bytes, sink, magic);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_write(void *dst, int64_t bytes, uint32_t value, hipStream_t s)
+{
+    const int64_t n16 = bytes / 16;
+    int64_t pieces = (n16 + kReadPiece - 1) / kReadPiece;
+    if (pieces > (1 << 20))
+        pieces = 1 << 20;
+    if (pieces < 1)
+        pieces = 1;
+    hipLaunchKernelGGL(probe_write_kernel, dim3((int)pieces), dim3(kBlock), 0, s, (u32x4 *)dst, n16,
+                       (uint8_t *)dst, bytes, value);
     return hipGetLastError();
 }
 

@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
                  "zero_gather_write", "zero_strerror", "zero_version", "zero_probe_copy",
-                 "zero_probe_read", "zero_shard_step_kahan", "zero_shard_step_bf16_moments"):
+                 "zero_probe_read", "zero_probe_write", "zero_shard_step_kahan",
+                 "zero_shard_step_bf16_moments"):
         assert name in fns
 
 
@@ -49,7 +50,7 @@ def test_library_exports_every_declared_symbol(zs):
 
 
 def test_version_and_strerror(zs):
-    assert zs.zero_version() == (1, 4)
+    assert zs.zero_version() == (1, 5)
     for code in range(8):
         assert zs.zero_strerror(code) and zs.zero_strerror(code) != "unknown error code"
     assert zs.zero_strerror(99) == "unknown error code"
@@ -159,6 +160,7 @@ def test_empty_calls_are_noops(zs):
     assert zs.raw_call("zero_gather_write", None, 0, None, 0, None) == zs.ZERO_OK
     assert zs.raw_call("zero_probe_copy", None, None, 0, None) == zs.ZERO_OK
     assert zs.raw_call("zero_probe_read", None, 0, None, 0, None) == zs.ZERO_OK
+    assert zs.raw_call("zero_probe_write", None, 0, 0, None) == zs.ZERO_OK
 
 
 def test_unfused_argument_errors(zs):
@@ -180,6 +182,10 @@ def test_unfused_argument_errors(zs):
     assert zs.raw_call("zero_probe_read", a, 64, None, 0, None) == zs.ZERO_ERR_INVALID
     assert zs.raw_call("zero_probe_read", a + 8, 64, a, 0, None) == zs.ZERO_ERR_MISALIGNED
     assert zs.raw_call("zero_probe_read", a, 64, a + 2, 0, None) == zs.ZERO_ERR_MISALIGNED
+    assert zs.raw_call("zero_probe_write", a, -16, 0, None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_probe_write", None, 64, 0, None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_probe_write", a + 8, 64, 0, None) == zs.ZERO_ERR_MISALIGNED
+    assert zs.raw_call("zero_probe_write", a, 64, 0, None) == zs.ZERO_ERR_NOT_DEVICE
 
 
 # ---------------------------------------------------------------- chunk table

@@ -116,3 +116,13 @@ def test_code_hash_ignores_comments_not_code():
     assert bench.code_text(a) == bench.code_text(b)
     assert bench.code_text(a) != bench.code_text(c)
     assert bench.code_text(a) != bench.code_text(d)
+
+
+def test_mix_bound():
+    """Reads at r, writes at w, one after the other: pure streams give their
+    own rate; a 2:1 mix lies between, nearer the read rate."""
+    assert bench.mix_bound(100, 0, 6.6, 5.7) == pytest.approx(6.6)
+    assert bench.mix_bound(0, 100, 6.6, 5.7) == pytest.approx(5.7)
+    b = bench.mix_bound(28, 14, 6600.0, 5700.0)
+    assert b == pytest.approx(42 / (28 / 6600 + 14 / 5700))
+    assert 5700 < b < 6600
