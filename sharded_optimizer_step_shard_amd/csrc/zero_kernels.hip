@@ -29,7 +29,7 @@
 
 namespace zs {
 
-constexpr int kBlock = 256;       // grid-stride kernels (unfused, probe)
+constexpr int kBlock = 256;       // grid-stride kernels (unfused path)
 constexpr int kStepBlock = 64;    // chunk-table kernels: one wave per workgroup
 
 // Native clang vectors: 16-byte (and 8-byte) loads and stores, and the
@@ -787,67 +787,6 @@ void gather_kernel(GatherArgs a)
         gather_chunk(a, chunk_at(a.chunks, ci));
 }
 
-__global__ __launch_bounds__(kBlock) void probe_copy_kernel(const u32x4 *src, u32x4 *dst, int64_t n16,
-                                                            const uint8_t *src_b, uint8_t *dst_b,
-                                                            int64_t bytes)
-{
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n16; i += (int64_t)gridDim.x * kBlock)
-        st_nt(dst + i, ld(src + i));
-    if (blockIdx.x == 0) {
-        const int64_t b = n16 * 16 + threadIdx.x;
-        if (b < bytes)
-            dst_b[b] = src_b[b];
-    }
-}
-
-// Read-only stream: workgroup b reads 4 KiB pieces b, b + gridDim.x, ...
-// (one 16-byte load per lane), folding them by XOR into a value that is
-// stored only if it equals `magic`, so the loads cannot be dropped and in
-// practice nothing is written.  Many short contiguous pieces per workgroup
-// sustained the highest read rate among the shapes measured on MI355X.
-constexpr int kReadPiece = kBlock;     // 16-byte words per piece (4 KiB)
-
-__global__ __launch_bounds__(kBlock) void probe_read_kernel(const u32x4 *src, int64_t n16,
-                                                            const uint8_t *src_b, int64_t bytes,
-                                                            uint32_t *sink, uint32_t magic)
-{
-    u32x4 acc = {0u, 0u, 0u, 0u};
-    for (int64_t p = blockIdx.x; p * kReadPiece < n16; p += gridDim.x) {
-        const int64_t i = p * kReadPiece + threadIdx.x;
-        if (i < n16)
-            acc ^= ld(src + i);
-    }
-    uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
-    if (blockIdx.x == 0) {
-        const int64_t b = n16 * 16 + threadIdx.x;
-        if (b < bytes)
-            x ^= src_b[b];
-    }
-    if (x == magic)
-        sink[0] = x;
-}
-
-// Write-only stream: workgroup b writes 4 KiB pieces b, b + gridDim.x, ...
-// with one non-temporal 16-byte store per lane (the store the step kernels
-// use for their state), the bytes past the last full word element by
-// element.  The value written is `value` in every 32-bit word.
-__global__ __launch_bounds__(kBlock) void probe_write_kernel(u32x4 *dst, int64_t n16,
-                                                             uint8_t *dst_b, int64_t bytes,
-                                                             uint32_t value)
-{
-    const u32x4 w = {value, value, value, value};
-    for (int64_t p = blockIdx.x; p * kReadPiece < n16; p += gridDim.x) {
-        const int64_t i = p * kReadPiece + threadIdx.x;
-        if (i < n16)
-            st_nt(dst + i, w);
-    }
-    if (blockIdx.x == 0) {
-        const int64_t b = n16 * 16 + threadIdx.x;
-        if (b < bytes)
-            dst_b[b] = (uint8_t)value;
-    }
-}
-
 // ---------------------------------------------------------------- launchers
 
 static int grid_for(int64_t items)
@@ -1053,41 +992,6 @@ hipError_t launch_adamw(const AdamArgs &a, hipStream_t s)
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s)
 {
     hipLaunchKernelGGL(gather_kernel, dim3(chunk_grid(a.n_chunks)), dim3(kStepBlock), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s)
-{
-    const int64_t n16 = bytes / 16;
-    hipLaunchKernelGGL(probe_copy_kernel, dim3(grid_for(n16 + 1)), dim3(kBlock), 0, s,
-                       (const u32x4 *)src, (u32x4 *)dst, n16, (const uint8_t *)src, (uint8_t *)dst, bytes);
-    return hipGetLastError();
-}
-
-hipError_t launch_probe_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t magic,
-                             hipStream_t s)
-{
-    const int64_t n16 = bytes / 16;
-    int64_t pieces = (n16 + kReadPiece - 1) / kReadPiece;
-    if (pieces > (1 << 20))
-        pieces = 1 << 20;
-    if (pieces < 1)
-        pieces = 1;
-    hipLaunchKernelGGL(probe_read_kernel, dim3((int)pieces), dim3(kBlock), 0, s, (const u32x4 *)src,
-                       n16, (const uint8_t *)src, bytes, sink, magic);
-    return hipGetLastError();
-}
-
-hipError_t launch_probe_write(void *dst, int64_t bytes, uint32_t value, hipStream_t s)
-{
-    const int64_t n16 = bytes / 16;
-    int64_t pieces = (n16 + kReadPiece - 1) / kReadPiece;
-    if (pieces > (1 << 20))
-        pieces = 1 << 20;
-    if (pieces < 1)
-        pieces = 1;
-    hipLaunchKernelGGL(probe_write_kernel, dim3((int)pieces), dim3(kBlock), 0, s, (u32x4 *)dst, n16,
-                       (uint8_t *)dst, bytes, value);
     return hipGetLastError();
 }
 
