@@ -72,3 +72,35 @@ def kahan_step_bytes_per_param(n_ranks: int, grad_bytes: int = 2) -> int:
     partials read; parameter, compensation, m, v (bf16 each) read and
     written."""
     return n_ranks * grad_bytes + 2 * (2 + 2 + 2 + 2)
+
+
+# ---- communication volumes ---------------------------------------------------
+# Ring collectives over a buffer of M elements on n ranks ("并行策略总览：六个维度
+# 各切什么、怎么通信", collectives table): all-reduce sends 2(n-1)M/n elements per
+# rank, reduce-scatter, all-gather and all-to-all (n-1)M/n; and all-reduce =
+# reduce-scatter + all-gather.
+
+RING_FACTOR = {"all-reduce": 2, "reduce-scatter": 1, "all-gather": 1, "all-to-all": 1}
+
+
+def ring_volume(collective: str, n_ranks: int, m: float) -> float:
+    """Elements each rank sends in a ring `collective` over m elements."""
+    return RING_FACTOR[collective] * (n_ranks - 1) * m / n_ranks
+
+
+def step_volume(stage: int, n_ranks: int, psi: float) -> float:
+    """Elements each rank sends per optimizer step for a model of psi
+    parameters (same page, data-parallel section): plain data parallelism
+    all-reduces the gradient; ZeRO-1/2 reduce-scatter it and all-gather the
+    updated parameters, the same volume (about 2 psi); ZeRO-3 also
+    all-gathers the parameters a second time, for the backward pass (about
+    3 psi)."""
+    rs = ring_volume("reduce-scatter", n_ranks, psi)
+    ag = ring_volume("all-gather", n_ranks, psi)
+    if stage == 0:
+        return ring_volume("all-reduce", n_ranks, psi)
+    if stage in (1, 2):
+        return rs + ag
+    if stage == 3:
+        return rs + 2 * ag
+    raise ValueError(stage)
