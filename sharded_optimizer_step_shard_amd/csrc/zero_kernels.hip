@@ -215,15 +215,16 @@ __device__ __forceinline__ u32x4 ld_raw(const void *base, int64_t byte_off)
 }
 
 // Sum of the N partials over one full group starting at element i0, in
-// rank order.  NC > 0: N known at compile time (loads issued in batches of
-// up to 16 before their adds); NC == 0: N at run time.
-template <zero_dtype G, int NC>
+// rank order.  NC > 0: N known at compile time, the loads issued in batches
+// of up to BATCH before their adds (the batch changes how many loads are in
+// flight, never the order of the sum); NC == 0: N at run time.
+template <zero_dtype G, int NC, int BATCH = 16>
 __device__ __forceinline__ void group_sum(double *s, const PartialPtrs &pp, int n_rt, int64_t i0)
 {
     using GT = Grad<G>;
     const int64_t off = i0 * GT::BYTES;
     if constexpr (NC > 0) {
-        constexpr int B = NC < 16 ? NC : 16;
+        constexpr int B = NC < BATCH ? NC : BATCH;
 #pragma unroll
         for (int kb = 0; kb < NC; kb += B) {
             u32x4 raw[B];
@@ -297,7 +298,7 @@ __device__ __forceinline__ void fold_finish(double *s, const double *t, int n, i
 
 // KC > 0: group size known at compile time, so after unrolling every group
 // boundary test folds away; KC == 0: K at run time (scalar branches).
-template <zero_dtype G, int NC, int KC>
+template <zero_dtype G, int NC, int KC, int BATCH = 16>
 __device__ __forceinline__ void group_sum_two_level(double *s, const PartialPtrs &pp, int n_rt,
                                                     int K_rt, int64_t i0)
 {
@@ -307,7 +308,7 @@ __device__ __forceinline__ void group_sum_two_level(double *s, const PartialPtrs
     const int64_t off = i0 * GT::BYTES;
     double t[VEC];
     if constexpr (NC > 0) {
-        constexpr int B = NC < 16 ? NC : 16;
+        constexpr int B = NC < BATCH ? NC : BATCH;
 #pragma unroll
         for (int kb = 0; kb < NC; kb += B) {
             u32x4 raw[B];
@@ -418,6 +419,14 @@ __device__ __forceinline__ void store_bf16(uint16_t *dst, const uint32_t *h, boo
 
 // ---------------------------------------------------------------- fused step
 
+// Partial loads in flight per batch (group_sum) for each fused step, from
+// in-process sweeps on MI355X (bitwise-equal results): batches of 8 beat 16
+// for the one-wave 16-byte step with 16 or 32 partials (70B: +1-4%, 32 fp32
+// partials: +1%); the 12-byte step running two waves per SIMD does best
+// with batches of 2 (7B: 0.665 -> 0.684 of peak); the pure-bf16 step keeps
+// 16 (smaller batches were up to 3% slower at 70B).
+constexpr int kStepBatch = 8;
+
 // EXT: the extended reduce of zero_shard_step_ex (two-level order, optional
 // accumulator of earlier micro-batches, divisor N * micro-batches).
 template <zero_dtype G, int NC, bool EXT, int KC>
@@ -446,16 +455,16 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
                 if (a.acc)
                     acc.load(a.acc + i0);
                 if constexpr (KC < 0)
-                    group_sum<G, NC>(s, a.parts, n, i0);
+                    group_sum<G, NC, kStepBatch>(s, a.parts, n, i0);
                 else
-                    group_sum_two_level<G, NC, KC>(s, a.parts, n, a.red.group, i0);
+                    group_sum_two_level<G, NC, KC, kStepBatch>(s, a.parts, n, a.red.group, i0);
                 if (a.acc) {
 #pragma unroll
                     for (int j = 0; j < VEC; ++j)
                         s[j] = (double)acc[j] + s[j];
                 }
             } else {
-                group_sum<G, NC>(s, a.parts, n, i0);
+                group_sum<G, NC, kStepBatch>(s, a.parts, n, i0);
             }
             uint32_t h[VEC];
 #pragma unroll
@@ -493,6 +502,21 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
     }
 }
 
+// Resident waves per SIMD of the 12-byte and pure-bf16 steps.  Both do more
+// arithmetic per byte moved than the 16-byte step (bf16 moments rounded from
+// double; the compensated update on top), and when the N partials are few
+// bytes per element one wave per SIMD leaves the memory pipe idle during its
+// arithmetic.  Measured on MI355X (7B shard, N = 8 bf16): the 12-byte step
+// 0.65 -> 0.67 of HBM peak with two waves, the pure-bf16 step 0.47 -> 0.655
+// with three; with 16 partials (70B) the 12-byte step is best with one wave
+// (0.725 against 0.69), the pure-bf16 step with two (0.63 -> 0.71; its
+// registers allow no third).
+template <zero_dtype G, int NC>
+constexpr int kM16Waves = (NC > 0 && NC * Grad<G>::BYTES <= 16) ? 2 : 1;
+constexpr int kKahanWaves = 3;
+template <zero_dtype G, int NC>
+constexpr int kM16Batch = kM16Waves<G, NC> == 2 ? 2 : kStepBatch;
+
 // The step on the 12-byte state: fp32 master, bf16 m and v (in a.m, a.v
 // as 16-bit patterns).  Same reduce and AdamW; the moments are read from
 // bf16 and rounded back to bf16 once, from double.
@@ -517,7 +541,7 @@ __device__ __forceinline__ void step_chunk_m16(const StepArgs &a, const zero_chu
             th.load(a.master + i0);
             m.load(m16 + i0);
             v.load(v16 + i0);
-            group_sum<G, NC>(s, a.parts, n, i0);
+            group_sum<G, NC, kM16Batch<G, NC>>(s, a.parts, n, i0);
             uint32_t h[VEC];
 #pragma unroll
             for (int j = 0; j < VEC; ++j) {
@@ -549,19 +573,6 @@ __device__ __forceinline__ void step_chunk_m16(const StepArgs &a, const zero_chu
         }
     }
 }
-
-// Resident waves per SIMD of the 12-byte and pure-bf16 steps.  Both do more
-// arithmetic per byte moved than the 16-byte step (bf16 moments rounded from
-// double; the compensated update on top), and when the N partials are few
-// bytes per element one wave per SIMD leaves the memory pipe idle during its
-// arithmetic.  Measured on MI355X (7B shard, N = 8 bf16): the 12-byte step
-// 0.65 -> 0.67 of HBM peak with two waves, the pure-bf16 step 0.47 -> 0.655
-// with three; with 16 partials (70B) the 12-byte step is best with one wave
-// (0.725 against 0.69), the pure-bf16 step with two (0.63 -> 0.71; its
-// registers allow no third).
-template <zero_dtype G, int NC>
-constexpr int kM16Waves = (NC > 0 && NC * Grad<G>::BYTES <= 16) ? 2 : 1;
-constexpr int kKahanWaves = 3;
 
 // The pure-bf16 step: the parameters are read from and written back to
 // the chunk's destination (the bf16 parameter is the only copy of the
