@@ -282,6 +282,24 @@ class Shard:
         return (self.w.n_ranks * (2 if self.w.gdt == "bf16" else 4) + rd + wr) * self.n
 
 
+def bucket_chunk_len(bucket_params: int) -> int:
+    """Chunk length for a step launched per bucket of about bucket_params
+    elements: bucket_params / 1024 rounded down to a power of two, within
+    [512, 2048].  A launch's waves each walk their chunk in groups of 512
+    elements (64 lanes x 8), one memory round trip per group, so a small
+    bucket cut into 2048-element chunks is a few latency-bound waves; about
+    a thousand chunks per bucket keeps the round trips in parallel.  Measured
+    on MI355X (7B shard, replayed from a HIP graph): 262K-element buckets
+    12.2 -> 6.4 us per launch with 512-element chunks, 1M-element buckets
+    16.2 -> 13.7 us with 1024; from 4M on, 2048 stays best."""
+    if bucket_params <= 0:
+        raise ValueError("bucket_params must be positive")
+    c = 2048
+    while c > 512 and c * 1024 > bucket_params:
+        c //= 2
+    return c
+
+
 def bucket_runs(chunk_lens, bucket_params: int) -> list:
     """Split a chunk table (its len column) into contiguous runs of whole
     chunks holding at least bucket_params elements each (the last run may
@@ -408,7 +426,8 @@ def probe_read(nbytes: int, reps: int = 5) -> dict:
             "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
-def launch_overhead(n_ranks: int = 8, n: int = 1 << 16, calls: int = 4000) -> dict:
+def launch_overhead(n_ranks: int = 8, n: int = 1 << 16, calls: int = 4000,
+                    max_chunk: int = None) -> dict:
     """Per-call cost of zero_shard_step on a small shard (n elements, 32
     chunks): the C call through ctypes with no chunks (argument checks only),
     the full C call (checks, one device-range query per array, launch; host
@@ -420,7 +439,8 @@ def launch_overhead(n_ranks: int = 8, n: int = 1 << 16, calls: int = 4000) -> di
     parts = [torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(n_ranks)]
     master, m, v = (torch.zeros(n, device="cuda") for _ in range(3))
     slot = torch.zeros(n, dtype=torch.int16, device="cuda")
-    table, _ = zs.zero_build_chunks([n], 1, 0, slot_dst=slot)
+    table, _ = zs.zero_build_chunks([n], 1, 0, slot_dst=slot,
+                                    max_chunk=max_chunk or zs.ZERO_DEFAULT_MAX_CHUNK)
     d_table = zs.chunks_to_device(table)
     hp = zs.hparams(3)
     stream = torch.cuda.current_stream().cuda_stream
@@ -446,9 +466,29 @@ def launch_overhead(n_ranks: int = 8, n: int = 1 << 16, calls: int = 4000) -> di
     c_issue, c_done = per_call(lambda: lib.zero_shard_step(*full))
     py_issue, py_done = per_call(lambda: zs.zero_shard_step(parts, master, m, v, n, d_table,
                                                             len(table), hp))
+    # the same launches captured in a HIP graph and replayed: GPU time per launch
+    in_graph, replays = 500, 10
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(in_graph):
+                zs.zero_shard_step(parts, master, m, v, n, d_table, len(table), hp)
+    torch.cuda.current_stream().wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / (in_graph * replays)
     return {"elements": n, "chunks": len(table), "n_ranks": n_ranks, "calls": calls,
             "c_checks_only_us": checks, "c_full_issue_us": c_issue, "c_full_with_gpu_us": c_done,
-            "python_issue_us": py_issue, "python_with_gpu_us": py_done}
+            "python_issue_us": py_issue, "python_with_gpu_us": py_done,
+            "graph_replay_per_launch_us": graph_us}
 
 
 def probe_write(nbytes: int, reps: int = 5) -> dict:
@@ -620,6 +660,10 @@ def main() -> int:
     ap.add_argument("--bucket-params", type=int, default=0,
                     help="step the shard in buckets of about this many params, one launch "
                          "per bucket (ZeRO-2 bucketed step); 0 = one launch per step")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step's launches in a HIP graph and time its replays "
+                         "(the hyper-parameters, step t included, are fixed at capture; the "
+                         "work per replay is the step's)")
     ap.add_argument("--probe-copy", type=int, default=1 << 32, metavar="BYTES",
                     help="after timing, copy BYTES with the library's plain copy kernel "
                          "(measured copy bandwidth of this GPU; the known-size kernel that "
@@ -639,7 +683,7 @@ def main() -> int:
         print(trace_summary(args.trace_summary))
         return 0
     if args.launch_overhead:
-        print(json.dumps(launch_overhead()), flush=True)
+        print(json.dumps(launch_overhead(max_chunk=args.max_chunk)), flush=True)
         return 0
     if args.ingest_counters:
         rec = ingest_counters(*args.ingest_counters, W.get(args.workload), args.rank, args.state,
@@ -656,7 +700,10 @@ def main() -> int:
     import torch
 
     w = W.get(args.workload)
-    sh = Shard(w, args.rank, args.dst, args.max_chunk)
+    max_chunk = args.max_chunk
+    if max_chunk is None and args.bucket_params > 0:
+        max_chunk = bucket_chunk_len(args.bucket_params)
+    sh = Shard(w, args.rank, args.dst, max_chunk)
     t = sh.prepare()
     torch.cuda.synchronize()
     print(f"# {w.name}: shard {sh.n} params, N={w.n_ranks} {w.gdt}, {len(sh.table)} chunks, "
@@ -681,6 +728,15 @@ def main() -> int:
     elif extended:
         sh.set_extended(args.group, args.micro_batches)
         step = sh.step_extended
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                step(t)
+        torch.cuda.current_stream().wait_stream(side)
+        step = lambda _t: graph.replay()        # noqa: E731
     for _ in range(args.warmup):
         step(t)
         t += 1
@@ -747,6 +803,8 @@ def main() -> int:
                    "dst": sh.dst_mode, "bytes_per_param": sh.bytes_per_launch() // sh.n,
                    "state": args.state,
                    "launches_per_step": launches,
+                   "max_chunk": int(sh.table["len"].max()) if len(sh.table) else 0,
+                   "graph_replay": bool(args.graph),
                    "parallelism": "one data-parallel rank's ZeRO shard"},
         "hbm_gbs": achieved,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

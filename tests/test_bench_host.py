@@ -126,3 +126,14 @@ def test_mix_bound():
     b = bench.mix_bound(28, 14, 6600.0, 5700.0)
     assert b == pytest.approx(42 / (28 / 6600 + 14 / 5700))
     assert 5700 < b < 6600
+
+
+def test_bucket_chunk_len():
+    assert bench.bucket_chunk_len(262_144) == 512
+    assert bench.bucket_chunk_len(1 << 20) == 1024
+    assert bench.bucket_chunk_len(3_000_000) == 2048
+    assert bench.bucket_chunk_len(1 << 26) == 2048
+    assert bench.bucket_chunk_len(1000) == 512
+    for p in (1, 10**5, 10**6, 10**7, 10**9):
+        c = bench.bucket_chunk_len(p)
+        assert c in (512, 1024, 2048) and c % 64 == 0
