@@ -36,8 +36,11 @@ import synth  # noqa: E402
 from synth import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+# What decides the step kernels' HBM traffic: the kernels, their argument
+# layout, and how the chunk table is cut.  Recorded counters stay valid while
+# the code (not the comments) of these files is unchanged.
 KERNEL_SOURCES = [os.path.join(ROOT, "sharded_optimizer_step_shard_amd", "csrc", f)
-                  for f in ("zero_kernels.hip", "zero_api.cpp", "zero_internal.h")]
+                  for f in ("zero_kernels.hip", "zero_internal.h", "zero_chunks.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # Optimizer-state layouts the fused step runs on: the kernel, the state bytes
@@ -253,6 +256,14 @@ class Shard:
         return self.buckets
 
     def step_bucketed(self, t: int) -> None:
+        """All buckets enqueued by one call (zero_shard_step_buckets)."""
+        self.zs.zero_shard_step_buckets(self.partials, self.master, self.m, self.v, self.n,
+                                        self.d_table, len(self.table), self.buckets,
+                                        self.zs.hparams(t, **self.w.hparams()))
+        self.step_t = t
+
+    def step_bucketed_loop(self, t: int) -> None:
+        """One zero_shard_step call per bucket from Python."""
         hp = self.zs.hparams(t, **self.w.hparams())
         base = self.d_table.data_ptr()
         for first, count in self.buckets:
@@ -660,6 +671,9 @@ def main() -> int:
     ap.add_argument("--bucket-params", type=int, default=0,
                     help="step the shard in buckets of about this many params, one launch "
                          "per bucket (ZeRO-2 bucketed step); 0 = one launch per step")
+    ap.add_argument("--bucket-call", default="one", choices=["one", "per-bucket"],
+                    help="with --bucket-params: enqueue all buckets with one "
+                         "zero_shard_step_buckets call, or call zero_shard_step per bucket")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step's launches in a HIP graph and time its replays "
                          "(the hyper-parameters, step t included, are fixed at capture; the "
@@ -724,7 +738,7 @@ def main() -> int:
             step = sh.step_kahan
     if args.bucket_params > 0:
         sh.set_buckets(args.bucket_params)
-        step = sh.step_bucketed
+        step = sh.step_bucketed if args.bucket_call == "one" else sh.step_bucketed_loop
     elif extended:
         sh.set_extended(args.group, args.micro_batches)
         step = sh.step_extended
@@ -805,6 +819,7 @@ def main() -> int:
                    "launches_per_step": launches,
                    "max_chunk": int(sh.table["len"].max()) if len(sh.table) else 0,
                    "graph_replay": bool(args.graph),
+                   "bucket_call": args.bucket_call if args.bucket_params > 0 else None,
                    "parallelism": "one data-parallel rank's ZeRO shard"},
         "hbm_gbs": achieved,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

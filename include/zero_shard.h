@@ -173,6 +173,32 @@ int zero_shard_step(const void *const *partials, int n_ranks, int gdt,
                     const zero_adamw_hparams *hp, hipStream_t stream);
 
 /*
+ * The fused step in buckets (ZeRO-2: "并行训练优化、MoE扩展与系统瓶颈", 2.2.4,
+ * and "CS336 2026 Lecture 8: Parallelism Basics", the ZeRO-2 slides: each
+ * gradient bucket is reduce-scattered as soon as it is complete, so its
+ * slice of the shard can be stepped without waiting for the others).  One
+ * call checks the whole shard as zero_shard_step does, then enqueues one
+ * step launch per bucket on `stream`: bucket b covers chunks
+ * [first[b], first[b] + count[b]) of d_chunks.  If `ready` is not NULL
+ * and ready[b] is not NULL, the stream first waits for event ready[b] (for
+ * example an event recorded when that bucket's gradients have arrived), so
+ * the host can enqueue a whole overlapped step at once.
+ * first, count, ready: host arrays of n_buckets entries.  Buckets must be
+ * in increasing order, disjoint and inside the table (INVALID otherwise);
+ * chunks outside every bucket are not stepped.  The result equals
+ * zero_shard_step over the buckets' chunks, bit for bit.  Errors as
+ * zero_shard_step; every non-NULL event is probed with hipEventQuery
+ * before anything is enqueued, and an invalid one gives HIP with nothing
+ * launched.
+ */
+int zero_shard_step_buckets(const void *const *partials, int n_ranks, int gdt,
+                            float *master, float *m, float *v, int64_t shard_len,
+                            const zero_chunk *d_chunks, int64_t n_chunks,
+                            const int64_t *first, const int64_t *count, int n_buckets,
+                            const hipEvent_t *ready, const zero_adamw_hparams *hp,
+                            hipStream_t stream);
+
+/*
  * Extended reduce for data-parallel layouts beyond one flat group and for
  * more than one micro-batch per optimizer step.
  *

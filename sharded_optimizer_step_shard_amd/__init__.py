@@ -69,6 +69,8 @@ _lib.zero_build_chunks.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp, _
                                    ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
 _lib.zero_shard_step.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64,
                                  ctypes.POINTER(HParams), _vp]
+_lib.zero_shard_step_buckets.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp,
+                                         _i32, _vp, ctypes.POINTER(HParams), _vp]
 _lib.zero_shard_step_ex.argtypes = [_vp, _i32, _i32, ctypes.POINTER(ReduceSpec), _vp, _vp, _vp,
                                     _i64, _vp, _i64, ctypes.POINTER(HParams), _vp]
 _lib.zero_accumulate_shard.argtypes = [_vp, _i32, _i32, _i32, _i64, _vp, _i32, _vp]
@@ -87,7 +89,8 @@ _lib.zero_strerror.restype = ctypes.c_char_p
 for _f in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
            "zero_gather_write", "zero_probe_copy", "zero_probe_read", "zero_probe_write",
            "zero_version", "zero_shard_step_ex",
-           "zero_accumulate_shard", "zero_shard_step_bf16_moments", "zero_shard_step_kahan"):
+           "zero_accumulate_shard", "zero_shard_step_bf16_moments", "zero_shard_step_kahan",
+           "zero_shard_step_buckets"):
     getattr(_lib, _f).restype = _i32
 
 Ptr = Union[int, "torch.Tensor", None]  # noqa: F821
@@ -186,6 +189,30 @@ def zero_shard_step(partials: Sequence[Ptr], master: Ptr, m: Ptr, v: Ptr, shard_
     _check(_lib.zero_shard_step(_partial_array(partials), len(partials), gdt, _addr(master),
                                 _addr(m), _addr(v), shard_len, _addr(d_chunks), n_chunks,
                                 ctypes.byref(hp), _stream(stream)), "zero_shard_step")
+
+
+def zero_shard_step_buckets(partials: Sequence[Ptr], master: Ptr, m: Ptr, v: Ptr, shard_len: int,
+                            d_chunks: Ptr, n_chunks: int, runs: Sequence[Tuple[int, int]],
+                            hp: HParams, ready=None, gdt: Optional[int] = None,
+                            stream=None) -> None:
+    """The fused step in buckets, one C call: runs = [(first chunk, chunk
+    count), ...] in increasing, disjoint order; ready = per-bucket events
+    (torch.cuda.Event or None) the stream waits for before each bucket."""
+    gdt = _gdt_of(partials) if gdt is None else gdt
+    nb = len(runs)
+    first = np.ascontiguousarray([r[0] for r in runs], dtype=np.int64)
+    count = np.ascontiguousarray([r[1] for r in runs], dtype=np.int64)
+    ev = None
+    if ready is not None:
+        if len(ready) != nb:
+            raise ValueError("one ready event (or None) per bucket")
+        ev = (ctypes.c_void_p * max(nb, 1))(*[None if e is None else e.cuda_event for e in ready])
+    _check(_lib.zero_shard_step_buckets(_partial_array(partials), len(partials), gdt, _addr(master),
+                                        _addr(m), _addr(v), shard_len, _addr(d_chunks), n_chunks,
+                                        first.ctypes.data if nb else None,
+                                        count.ctypes.data if nb else None, nb, ev,
+                                        ctypes.byref(hp), _stream(stream)),
+           "zero_shard_step_buckets")
 
 
 def zero_shard_step_ex(partials: Sequence[Ptr], master: Ptr, m: Ptr, v: Ptr, shard_len: int,

@@ -4,8 +4,8 @@
 
 (run as a script: importing the package needs the library already built).
 
-compiles csrc/zero_kernels.hip, csrc/zero_probes.hip and csrc/zero_api.cpp for gfx950
-with hipcc.
+compiles csrc/zero_kernels.hip, csrc/zero_probes.hip, csrc/zero_chunks.cpp and
+csrc/zero_api.cpp for gfx950 with hipcc.
 Flags that matter for the results:
   -ffp-contract=off  no fused multiply-add: the double arithmetic of the step
                      must be the separately rounded operations it is defined as.
@@ -41,7 +41,8 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = True, out: str = LIB, extra=()) -> str:
-    srcs = [os.path.join(CSRC, f) for f in ("zero_kernels.hip", "zero_probes.hip", "zero_api.cpp")]
+    srcs = [os.path.join(CSRC, f)
+            for f in ("zero_kernels.hip", "zero_probes.hip", "zero_chunks.cpp", "zero_api.cpp")]
     cmd = [hipcc(), *HIP_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-o", out, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -134,7 +134,7 @@ bool in_device_alloc(const void *p, int64_t bytes)
 
 extern "C" {
 
-int zero_version(void) { return (1 << 16) | 5; }
+int zero_version(void) { return (1 << 16) | 6; }
 
 const char *zero_strerror(int code)
 {
@@ -151,86 +151,18 @@ const char *zero_strerror(int code)
     }
 }
 
-int zero_build_chunks(const int64_t *numels, int n_tensors, int n_ranks, int rank,
-                      uint16_t *const *tensor_dst, uint16_t *slot_dst, int64_t max_chunk,
-                      zero_chunk *out, int64_t cap, int64_t *n_out, int64_t *shard_len_out)
-{
-    if (!numels || n_tensors < 1 || n_ranks < 1 || rank < 0 || rank >= n_ranks)
-        return ZERO_ERR_INVALID;
-    if (max_chunk <= 0 || max_chunk % 64 != 0 || max_chunk > (int64_t(1) << 24))
-        return ZERO_ERR_INVALID;
-    if (!tensor_dst && !slot_dst)
-        return ZERO_ERR_INVALID;
-    if (out && cap < 0)
-        return ZERO_ERR_INVALID;
-    int64_t total = 0;
-    for (int t = 0; t < n_tensors; ++t) {
-        if (numels[t] < 0 || (tensor_dst && numels[t] > 0 && !tensor_dst[t]))
-            return ZERO_ERR_INVALID;
-        total += numels[t];
-    }
-    const int64_t S = (total + n_ranks - 1) / n_ranks;
-    int64_t lo = (int64_t)rank * S, hi = lo + S;
-    if (lo > total) lo = total;
-    if (hi > total) hi = total;
+}  // extern "C"
 
-    int64_t count = 0;
-    auto emit = [&](int64_t soff, int64_t len, int t, int64_t toff, uint16_t *dst) {
-        if (out && count < cap) {
-            zero_chunk &c = out[count];
-            c.shard_off = soff;
-            c.len = (int32_t)len;
-            c.tensor_id = t;
-            c.tensor_off = toff;
-            c.dst = dst;
-        }
-        ++count;
-    };
-    if (tensor_dst) {
-        // One piece per tensor that meets [lo, hi), each cut at multiples
-        // of max_chunk in shard coordinates.
-        int64_t a = 0;
-        for (int t = 0; t < n_tensors && a < hi; ++t) {
-            const int64_t b = a + numels[t];
-            for (int64_t x = a > lo ? a : lo, y = b < hi ? b : hi; x < y;) {
-                const int64_t soff = x - lo;
-                int64_t end = lo + (soff / max_chunk + 1) * max_chunk;
-                if (end > y) end = y;
-                emit(soff, end - x, t, x - a, tensor_dst[t] + (x - a));
-                x = end;
-            }
-            a = b;
-        }
-    } else {
-        // Contiguous slot: cut only at multiples of max_chunk; record the
-        // tensor holding each chunk's first element.
-        int t = 0;
-        int64_t a = 0;
-        for (int64_t soff = 0; soff < hi - lo; soff += max_chunk) {
-            const int64_t x = lo + soff;
-            while (a + numels[t] <= x) {
-                a += numels[t];
-                ++t;
-            }
-            const int64_t len = (hi - x) < max_chunk ? (hi - x) : max_chunk;
-            emit(soff, len, t, x - a, slot_dst + soff);
-        }
-    }
-    if (n_out)
-        *n_out = count;
-    if (shard_len_out)
-        *shard_len_out = S;
-    if (out && count > cap)
-        return ZERO_ERR_CAPACITY;
-    return ZERO_OK;
-}
+namespace zs {
 
-int zero_shard_step(const void *const *partials, int n_ranks, int gdt,
-                    float *master, float *m, float *v, int64_t shard_len,
-                    const zero_chunk *d_chunks, int64_t n_chunks,
-                    const zero_adamw_hparams *hp, hipStream_t stream)
+// The checks of the 16-byte fused step, in the header's order, and its
+// kernel arguments.  Returns ZERO_OK with *empty set when there is nothing
+// to launch.
+static int prepare_step(const void *const *partials, int n_ranks, int gdt, float *master,
+                        float *m, float *v, int64_t shard_len, const zero_chunk *d_chunks,
+                        int64_t n_chunks, const zero_adamw_hparams *hp, StepArgs &a, bool *empty)
 {
-    StepArgs a{};
+    *empty = true;
     int rc = check_partials(partials, n_ranks, shard_len, a.parts);
     if (rc)
         return rc;
@@ -266,7 +198,72 @@ int zero_shard_step(const void *const *partials, int n_ranks, int gdt,
     a.chunks = d_chunks;
     a.n_chunks = n_chunks;
     a.shard_len = shard_len;
+    *empty = false;
+    return ZERO_OK;
+}
+
+}  // namespace zs
+
+extern "C" {
+
+int zero_shard_step(const void *const *partials, int n_ranks, int gdt,
+                    float *master, float *m, float *v, int64_t shard_len,
+                    const zero_chunk *d_chunks, int64_t n_chunks,
+                    const zero_adamw_hparams *hp, hipStream_t stream)
+{
+    StepArgs a{};
+    bool empty;
+    int rc = prepare_step(partials, n_ranks, gdt, master, m, v, shard_len, d_chunks, n_chunks, hp,
+                          a, &empty);
+    if (rc || empty)
+        return rc;
     return hip_status(launch_step(a, (zero_dtype)gdt, stream));
+}
+
+int zero_shard_step_buckets(const void *const *partials, int n_ranks, int gdt,
+                            float *master, float *m, float *v, int64_t shard_len,
+                            const zero_chunk *d_chunks, int64_t n_chunks,
+                            const int64_t *first, const int64_t *count, int n_buckets,
+                            const hipEvent_t *ready, const zero_adamw_hparams *hp,
+                            hipStream_t stream)
+{
+    if (n_buckets < 0 || (n_buckets > 0 && (!first || !count)))
+        return ZERO_ERR_INVALID;
+    int64_t end = 0;
+    for (int b = 0; b < n_buckets; ++b) {
+        if (count[b] < 0 || first[b] < end || first[b] > n_chunks - count[b])
+            return ZERO_ERR_INVALID;   // out of the table, overlapping or out of order
+        end = first[b] + count[b];
+    }
+    StepArgs a{};
+    bool empty;
+    int rc = prepare_step(partials, n_ranks, gdt, master, m, v, shard_len, d_chunks, n_chunks, hp,
+                          a, &empty);
+    if (rc || empty || n_buckets == 0)
+        return rc;
+    if (ready) {
+        for (int b = 0; b < n_buckets; ++b) {
+            if (!ready[b])
+                continue;
+            const hipError_t e = hipEventQuery(ready[b]);
+            if (e != hipSuccess && e != hipErrorNotReady) {
+                (void)hipGetLastError();
+                return ZERO_ERR_HIP;
+            }
+        }
+    }
+    for (int b = 0; b < n_buckets; ++b) {
+        if (count[b] == 0)
+            continue;
+        if (ready && ready[b] && hipStreamWaitEvent(stream, ready[b], 0) != hipSuccess)
+            return ZERO_ERR_HIP;
+        a.chunks = d_chunks + first[b];
+        a.n_chunks = count[b];
+        rc = hip_status(launch_step(a, (zero_dtype)gdt, stream));
+        if (rc)
+            return rc;
+    }
+    return ZERO_OK;
 }
 
 int zero_shard_step_ex(const void *const *partials, int n_ranks, int gdt,

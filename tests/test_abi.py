@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
                  "zero_gather_write", "zero_strerror", "zero_version", "zero_probe_copy",
-                 "zero_probe_read", "zero_probe_write", "zero_shard_step_kahan",
+                 "zero_probe_read", "zero_probe_write", "zero_shard_step_kahan", "zero_shard_step_buckets",
                  "zero_shard_step_bf16_moments"):
         assert name in fns
 
@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(zs):
 
 
 def test_version_and_strerror(zs):
-    assert zs.zero_version() == (1, 5)
+    assert zs.zero_version() == (1, 6)
     for code in range(8):
         assert zs.zero_strerror(code) and zs.zero_strerror(code) != "unknown error code"
     assert zs.zero_strerror(99) == "unknown error code"
@@ -315,3 +315,30 @@ def test_checks_run_in_the_documented_order(zs):
     assert zs.raw_call("zero_reduce_shard", p, 4, 9, 10, out, None) == E.ZERO_ERR_UNSUPPORTED
     assert zs.raw_call("zero_accumulate_shard", mis, 4, 9, 0, 10, out, 1, None) == E.ZERO_ERR_MISALIGNED
     assert zs.raw_call("zero_accumulate_shard", p, 4, 9, 0, 10, out, 1, None) == E.ZERO_ERR_UNSUPPORTED
+
+
+def buckets(zs, first, count, n_buckets=None, n_chunks=10, ready=None, **kw):
+    nb = len(first) if n_buckets is None else n_buckets
+    f = (ctypes.c_int64 * max(len(first), 1))(*first)
+    c = (ctypes.c_int64 * max(len(count), 1))(*count)
+    hp = zs.hparams(1)
+    return zs.raw_call("zero_shard_step_buckets", parts(4), 4, 0, BASE + (1 << 40),
+                       BASE + (1 << 40) + (1 << 32), BASE + (1 << 40) + (2 << 32), 1000,
+                       BASE + (1 << 41), n_chunks, f if first else None, c if count else None, nb,
+                       ready, ctypes.byref(hp), None)
+
+
+def test_bucket_step_argument_errors(zs):
+    """Bucket ranges are checked before anything else is: out of the table,
+    overlapping, out of order, negative, or missing arrays are INVALID; valid
+    buckets on fake addresses reach the device check (NOT_DEVICE)."""
+    E = zs
+    assert buckets(zs, [0, 5], [5, 5]) == E.ZERO_ERR_NOT_DEVICE
+    assert buckets(zs, [0, 6], [5, 4]) == E.ZERO_ERR_NOT_DEVICE       # a gap is allowed
+    assert buckets(zs, [0, 4], [5, 5]) == E.ZERO_ERR_INVALID          # overlap
+    assert buckets(zs, [5, 0], [5, 5]) == E.ZERO_ERR_INVALID          # out of order
+    assert buckets(zs, [0, 5], [5, 6]) == E.ZERO_ERR_INVALID          # past the table
+    assert buckets(zs, [0], [-1]) == E.ZERO_ERR_INVALID
+    assert buckets(zs, [], [], n_buckets=2) == E.ZERO_ERR_INVALID     # null arrays
+    assert buckets(zs, [], [], n_buckets=-1) == E.ZERO_ERR_INVALID
+    assert buckets(zs, [], [], n_buckets=0) == E.ZERO_ERR_NOT_DEVICE   # checks still run
