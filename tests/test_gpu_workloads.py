@@ -1,9 +1,12 @@
 """GPU parity at the workloads' real sizes, in the configuration bench.py
 times (its Shard setup: device-filled inputs, chunk table, launch).
 
-GPT-2 and the ragged fp32 case are compared in full; the 7B and 70B
-shards on sampled indices that the oracle replays one by one (every chunk
-boundary +-8, the first and last 4096 elements, 65,536 hashed indices).
+GPT-2, the ragged fp32 case and the 7B shard (every state layout) are
+compared in full, the 7B shard one slice of 2^26 elements at a time so that
+host memory stays small.  The 70B shard (4.4e9 elements, 203 GB of device
+inputs) is compared on sampled indices that the oracle replays one by one:
+every chunk boundary +-8, the first and last 4096 elements, 65,536 hashed
+indices and the indices around 2^32.
 """
 import gc
 
@@ -87,30 +90,71 @@ def test_ragged_fp32_full(bench):
     release()
 
 
-def test_llama7b_warm_start_and_sampled_steps(bench):
+SLICE = 1 << 26
+
+
+def shard_slices(n, size=SLICE):
+    for a in range(0, n, size):
+        yield a, min(n, a + size)
+
+
+def params_range(sh, a, b):
+    """bf16 bits the step wrote for shard elements [a, b)."""
+    if sh.dst_mode == "slot":
+        return host(sh.params[0][a:b])
+    starts = np.cumsum([0] + list(sh.w.numels))
+    g0, g1 = sh.lo + a, sh.lo + b
+    out = []
+    for t, p in enumerate(sh.params):
+        s, e = int(starts[t]), int(starts[t + 1])
+        lo, hi = max(s, g0), min(e, g1)
+        if lo < hi:
+            out.append(host(p[lo - s:hi - s]))
+    return np.concatenate(out)
+
+
+def warm_state(w, sh, prefix, a, b):
+    """The 7B shard's state after the warm start, for shard elements [a, b):
+    the prefix elements keep the oracle's own prefix run, later elements
+    take m, v from prefix element src(i) and their master from the
+    generator."""
+    pth, pm, pv = prefix
+    P = w.warm_prefix
+    idx = np.arange(a, b, dtype=np.int64)
+    src = synth.prefix_src(w.seed, synth.stream_id(synth.KIND_PREFIX_MAP), idx, P)
+    if b <= P:
+        th = pth[a:b].copy()
+    else:
+        th = host_master(w, sh.lo + idx)
+        if a < P:
+            th[:P - a] = pth[a:]
+    return idx, th, pm[src], pv[src]
+
+
+@pytest.mark.timeout(900)
+def test_llama7b_warm_start_then_full_compare(bench):
     w = W.llama7b()
     say(f"case: {w.name} rank 0: warm start ({w.warm_steps} steps on {w.warm_prefix}), "
-        "then 3 bench steps, sampled compare")
+        "then 3 bench steps, full compare")
     sh = bench.Shard(w, rank=0)
     t0 = sh.prepare()
     assert t0 == w.warm_steps + 1
     P = w.warm_prefix
-    pth, pm, pv = oracle_warm_prefix(w, sh.lo)
+    prefix = oracle_warm_prefix(w, sh.lo)
     say("  warm-start prefix: full compare against the oracle's own prefix run")
-    check_state((host(sh.master[:P]), host(sh.m[:P]), host(sh.v[:P])), (pth, pm, pv),
-                "7b warm prefix")
+    check_state((host(sh.master[:P]), host(sh.m[:P]), host(sh.v[:P])), prefix, "7b warm prefix")
     steps = [t0, t0 + 1, t0 + 2]
     for t in steps:
         sh.step(t)
-    idx = sample_indices(sh.table, sh.n, seed=7)
-    say(f"  {idx.size} sampled indices")
-    src = synth.prefix_src(w.seed, synth.stream_id(synth.KIND_PREFIX_MAP), idx, P)
-    th = np.where(idx < P, pth[np.minimum(idx, P - 1)], host_master(w, sh.lo + idx)).astype(np.float32)
-    m, v = pm[src].copy(), pv[src].copy()
-    parts = host_partials(w, t0, sh.lo + idx)     # the bench reuses step t0's partials
-    for t in steps:
-        th, m, v, p = oracle.shard_step(parts, th, m, v, oracle.hparams(t, **w.hparams()))
-    check_state(gather_state(sh, idx), (th, m, v, p), "7b sampled")
+    torch.cuda.synchronize()
+    for a, b in shard_slices(sh.n):
+        idx, th, m, v = warm_state(w, sh, prefix, a, b)
+        parts = host_partials(w, t0, sh.lo + idx)     # the bench reuses step t0's partials
+        for t in steps:
+            th, m, v, p = oracle.shard_step(parts, th, m, v, oracle.hparams(t, **w.hparams()))
+        check_state((host(sh.master[a:b]), host(sh.m[a:b]), host(sh.v[a:b]), params_range(sh, a, b)),
+                    (th, m, v, p), f"7b [{a}, {b})")
+        say(f"  [{a}, {b}) equal")
     del sh
     release()
 
@@ -173,59 +217,59 @@ def test_gpt2_kahan_full_five_steps(bench):
     release()
 
 
-def test_llama7b_kahan_sampled(bench):
+@pytest.mark.timeout(900)
+def test_llama7b_kahan_full(bench):
     """bench.py --state bf16-kahan on the 7B shard: warm start, switch to the
-    pure-bf16 state, three steps; sampled compare."""
+    pure-bf16 state, three steps; full compare."""
     w = W.llama7b()
-    say(f"case: {w.name} rank 0, warm start then pure-bf16 Kahan state, 3 steps, sampled")
+    say(f"case: {w.name} rank 0, warm start then pure-bf16 Kahan state, 3 steps, full compare")
     sh = bench.Shard(w, rank=0)
     t0 = sh.prepare()
     sh.use_kahan()
     steps = [t0, t0 + 1, t0 + 2]
     for t in steps:
         sh.step_kahan(t)
-    P = w.warm_prefix
-    pth, pm, pv = oracle_warm_prefix(w, sh.lo)
-    idx = sample_indices(sh.table, sh.n, seed=17)
-    say(f"  {idx.size} sampled indices")
-    src = synth.prefix_src(w.seed, synth.stream_id(synth.KIND_PREFIX_MAP), idx, P)
-    th32 = np.where(idx < P, pth[np.minimum(idx, P - 1)], host_master(w, sh.lo + idx)).astype(np.float32)
-    th, m, v = oracle.bf16_round(th32), oracle.bf16_round(pm[src]), oracle.bf16_round(pv[src])
-    c = np.zeros(idx.size, np.uint16)
-    parts = host_partials(w, t0, sh.lo + idx)     # the bench reuses step t0's partials
-    for t in steps:
-        th, c, m, v = oracle.shard_step_kahan(parts, th, c, m, v, oracle.hparams(t, **w.hparams()))
-    assert_kahan_state(gather_kahan(sh, idx), (th, c, m, v), "7b Kahan sampled")
+    torch.cuda.synchronize()
+    prefix = oracle_warm_prefix(w, sh.lo)
+    for a, b in shard_slices(sh.n):
+        idx, th32, m32, v32 = warm_state(w, sh, prefix, a, b)
+        th, m, v = oracle.bf16_round(th32), oracle.bf16_round(m32), oracle.bf16_round(v32)
+        c = np.zeros(idx.size, np.uint16)
+        parts = host_partials(w, t0, sh.lo + idx)     # the bench reuses step t0's partials
+        for t in steps:
+            th, c, m, v = oracle.shard_step_kahan(parts, th, c, m, v, oracle.hparams(t, **w.hparams()))
+        assert_kahan_state((params_range(sh, a, b), host(sh.comp[a:b]), host(sh.m[a:b]),
+                            host(sh.v[a:b])), (th, c, m, v), f"7b Kahan [{a}, {b})")
+        say(f"  [{a}, {b}) equal")
     del sh
     release()
 
 
-def test_llama7b_bf16_moments_sampled(bench):
+@pytest.mark.timeout(900)
+def test_llama7b_bf16_moments_full(bench):
     """bench.py --state bf16-moments on the 7B shard: warm start, moments
-    rounded to bf16, three steps; sampled compare."""
+    rounded to bf16, three steps; full compare."""
     w = W.llama7b()
-    say(f"case: {w.name} rank 0, warm start then 12-byte state, 3 steps, sampled")
+    say(f"case: {w.name} rank 0, warm start then 12-byte state, 3 steps, full compare")
     sh = bench.Shard(w, rank=0)
     t0 = sh.prepare()
     sh.use_bf16_moments()
     steps = [t0, t0 + 1, t0 + 2]
     for t in steps:
         sh.step_bf16_moments(t)
-    P = w.warm_prefix
-    pth, pm, pv = oracle_warm_prefix(w, sh.lo)
-    idx = sample_indices(sh.table, sh.n, seed=27)
-    say(f"  {idx.size} sampled indices")
-    src = synth.prefix_src(w.seed, synth.stream_id(synth.KIND_PREFIX_MAP), idx, P)
-    th = np.where(idx < P, pth[np.minimum(idx, P - 1)], host_master(w, sh.lo + idx)).astype(np.float32)
-    m, v = oracle.bf16_round(pm[src]), oracle.bf16_round(pv[src])
-    parts = host_partials(w, t0, sh.lo + idx)
-    for t in steps:
-        th, m, v, p = oracle.shard_step_bf16m(parts, th, m, v, oracle.hparams(t, **w.hparams()))
-    i = torch.from_numpy(idx).to(sh.dev)
-    assert_bitwise(sh.master[i].cpu().numpy(), th, "7b 12-byte master")
-    assert_bitwise(sh.m[i].cpu().numpy().view(np.uint16), m, "7b 12-byte m")
-    assert_bitwise(sh.v[i].cpu().numpy().view(np.uint16), v, "7b 12-byte v")
-    assert_bitwise(sh.param_at(idx), p, "7b 12-byte parameters")
+    torch.cuda.synchronize()
+    prefix = oracle_warm_prefix(w, sh.lo)
+    for a, b in shard_slices(sh.n):
+        idx, th, m32, v32 = warm_state(w, sh, prefix, a, b)
+        m, v = oracle.bf16_round(m32), oracle.bf16_round(v32)
+        parts = host_partials(w, t0, sh.lo + idx)
+        for t in steps:
+            th, m, v, p = oracle.shard_step_bf16m(parts, th, m, v, oracle.hparams(t, **w.hparams()))
+        assert_bitwise(host(sh.master[a:b]), th, f"7b 12-byte master [{a}, {b})")
+        assert_bitwise(host(sh.m[a:b]), m, f"7b 12-byte m [{a}, {b})")
+        assert_bitwise(host(sh.v[a:b]), v, f"7b 12-byte v [{a}, {b})")
+        assert_bitwise(params_range(sh, a, b), p, f"7b 12-byte parameters [{a}, {b})")
+        say(f"  [{a}, {b}) equal")
     del sh
     release()
 
