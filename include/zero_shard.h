@@ -67,6 +67,8 @@
  *     aligned (torch allocations are).  Lengths and offsets are arbitrary.
  *   - When the element count is 0 the call does nothing and its array
  *     pointers may be NULL (an empty shard).
+ *   - Element and byte counts above ZERO_MAX_LEN (2^48) are INVALID, so
+ *     that no byte size the library forms can overflow int64.
  */
 #ifndef ZERO_SHARD_H
 #define ZERO_SHARD_H
@@ -120,6 +122,7 @@ enum {
 };
 
 #define ZERO_MAX_RANKS 64
+#define ZERO_MAX_LEN (((int64_t)1) << 48)   /* largest element or byte count */
 #define ZERO_DEFAULT_MAX_CHUNK 2048   /* chunk length the step kernel is tuned for */
 
 /*
@@ -145,7 +148,9 @@ enum {
  * out: host array of cap chunks, or NULL to query the count only.
  * *n_out receives the number of chunks needed, *shard_len_out receives the
  * shard length S (both may be NULL).  Returns ZERO_ERR_CAPACITY if out is
- * not NULL and cap < *n_out (nothing written beyond cap).
+ * not NULL and cap < *n_out (nothing written beyond cap).  INVALID for a
+ * negative numel, a total above ZERO_MAX_LEN, a NULL destination of a
+ * non-empty tensor, rank outside [0, n_ranks) or a bad max_chunk.
  */
 int zero_build_chunks(const int64_t *numels, int n_tensors, int n_ranks, int rank,
                       uint16_t *const *tensor_dst, uint16_t *slot_dst, int64_t max_chunk,
@@ -163,8 +168,8 @@ int zero_build_chunks(const int64_t *numels, int n_tensors, int n_ranks, int ran
  *            [0, shard_len) are skipped.  Shard elements no chunk covers
  *            are left untouched.
  * hp:        host pointer to the hyper-parameters of this step.
- * Errors: INVALID (null, n_ranks out of range, shard_len < 0, n_chunks < 0,
- * bad hp), MISALIGNED, UNSUPPORTED (gdt), NOT_DEVICE, ALIAS (a partial overlaps master,
+ * Errors: INVALID (null, n_ranks out of range, shard_len < 0 or above
+ * ZERO_MAX_LEN, n_chunks < 0 or above INT32_MAX, bad hp), MISALIGNED, UNSUPPORTED (gdt), NOT_DEVICE, ALIAS (a partial overlaps master,
  * m or v, or those overlap each other), HIP.
  */
 int zero_shard_step(const void *const *partials, int n_ranks, int gdt,

@@ -27,6 +27,7 @@ ZERO_BF16, ZERO_FP32 = 0, 1
 ZERO_OK, ZERO_ERR_INVALID, ZERO_ERR_MISALIGNED, ZERO_ERR_UNSUPPORTED = 0, 1, 2, 3
 ZERO_ERR_ALIAS, ZERO_ERR_HIP, ZERO_ERR_CAPACITY, ZERO_ERR_NOT_DEVICE = 4, 5, 6, 7
 ZERO_MAX_RANKS = 64
+ZERO_MAX_LEN = 1 << 48          # largest element or byte count an entry point accepts
 ZERO_DEFAULT_MAX_CHUNK = 2048
 
 # Mirrors `zero_chunk` (32 bytes).

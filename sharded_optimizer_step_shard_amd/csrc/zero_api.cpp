@@ -16,6 +16,9 @@ namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// A count outside [0, ZERO_MAX_LEN]; below the limit count * 8 fits int64.
+bool bad_len(int64_t n) { return n < 0 || n > ZERO_MAX_LEN; }
+
 // [a, a + na) and [b, b + nb) (bytes) overlap?
 bool overlaps(const void *a, int64_t na, const void *b, int64_t nb)
 {
@@ -166,7 +169,7 @@ static int prepare_step(const void *const *partials, int n_ranks, int gdt, float
     int rc = check_partials(partials, n_ranks, shard_len, a.parts);
     if (rc)
         return rc;
-    if (((!master || !m || !v) && shard_len > 0) || shard_len < 0 || n_chunks < 0 ||
+    if (((!master || !m || !v) && shard_len > 0) || bad_len(shard_len) || n_chunks < 0 ||
         n_chunks > INT32_MAX ||
         (n_chunks > 0 && !d_chunks) || !valid_hparams(hp))
         return ZERO_ERR_INVALID;
@@ -227,7 +230,8 @@ int zero_shard_step_buckets(const void *const *partials, int n_ranks, int gdt,
                             const hipEvent_t *ready, const zero_adamw_hparams *hp,
                             hipStream_t stream)
 {
-    if (n_buckets < 0 || (n_buckets > 0 && (!first || !count)))
+    if (n_buckets < 0 || (n_buckets > 0 && (!first || !count)) || n_chunks < 0 ||
+        n_chunks > INT32_MAX)
         return ZERO_ERR_INVALID;
     int64_t end = 0;
     for (int b = 0; b < n_buckets; ++b) {
@@ -275,7 +279,7 @@ int zero_shard_step_ex(const void *const *partials, int n_ranks, int gdt,
     int rc = check_partials(partials, n_ranks, shard_len, a.parts);
     if (rc)
         return rc;
-    if (((!master || !m || !v) && shard_len > 0) || shard_len < 0 || n_chunks < 0 ||
+    if (((!master || !m || !v) && shard_len > 0) || bad_len(shard_len) || n_chunks < 0 ||
         n_chunks > INT32_MAX || (n_chunks > 0 && !d_chunks) || !valid_hparams(hp) ||
         !valid_reduce_spec(rs, n_ranks))
         return ZERO_ERR_INVALID;
@@ -324,7 +328,7 @@ int zero_shard_step_bf16_moments(const void *const *partials, int n_ranks, int g
     int rc = check_partials(partials, n_ranks, shard_len, a.parts);
     if (rc)
         return rc;
-    if (((!master || !m || !v) && shard_len > 0) || shard_len < 0 || n_chunks < 0 ||
+    if (((!master || !m || !v) && shard_len > 0) || bad_len(shard_len) || n_chunks < 0 ||
         n_chunks > INT32_MAX || (n_chunks > 0 && !d_chunks) || !valid_hparams(hp))
         return ZERO_ERR_INVALID;
     if (!partials_aligned(a.parts, n_ranks) || !aligned16(master) || !aligned16(m) ||
@@ -369,7 +373,7 @@ int zero_shard_step_kahan(const void *const *partials, int n_ranks, int gdt,
     int rc = check_partials(partials, n_ranks, shard_len, a.parts);
     if (rc)
         return rc;
-    if (((!comp || !m || !v) && shard_len > 0) || shard_len < 0 || n_chunks < 0 ||
+    if (((!comp || !m || !v) && shard_len > 0) || bad_len(shard_len) || n_chunks < 0 ||
         n_chunks > INT32_MAX || (n_chunks > 0 && !d_chunks) || !valid_hparams(hp))
         return ZERO_ERR_INVALID;
     if (!partials_aligned(a.parts, n_ranks) || !aligned16(comp) || !aligned16(m) ||
@@ -412,7 +416,7 @@ int zero_accumulate_shard(const void *const *partials, int n_ranks, int gdt, int
     int rc = check_partials(partials, n_ranks, n, a.parts);
     if (rc)
         return rc;
-    if ((!acc && n > 0) || n < 0 || group < 0 || group > n_ranks ||
+    if ((!acc && n > 0) || bad_len(n) || group < 0 || group > n_ranks ||
         (group > 0 && n_ranks % group != 0))
         return ZERO_ERR_INVALID;
     if (!partials_aligned(a.parts, n_ranks) || !aligned16(acc))
@@ -443,7 +447,7 @@ int zero_reduce_shard(const void *const *partials, int n_ranks, int gdt, int64_t
     int rc = check_partials(partials, n_ranks, n, a.parts);
     if (rc)
         return rc;
-    if ((!grad_out && n > 0) || n < 0)
+    if ((!grad_out && n > 0) || bad_len(n))
         return ZERO_ERR_INVALID;
     if (!partials_aligned(a.parts, n_ranks) || !aligned16(grad_out))
         return ZERO_ERR_MISALIGNED;
@@ -468,7 +472,7 @@ int zero_reduce_shard(const void *const *partials, int n_ranks, int gdt, int64_t
 int zero_adamw_shard(const float *grad, float *master, float *m, float *v, int64_t n,
                      const zero_adamw_hparams *hp, hipStream_t stream)
 {
-    if (((!grad || !master || !m || !v) && n > 0) || n < 0 || !valid_hparams(hp))
+    if (((!grad || !master || !m || !v) && n > 0) || bad_len(n) || !valid_hparams(hp))
         return ZERO_ERR_INVALID;
     if (!aligned16(grad) || !aligned16(master) || !aligned16(m) || !aligned16(v))
         return ZERO_ERR_MISALIGNED;
@@ -494,7 +498,7 @@ int zero_adamw_shard(const float *grad, float *master, float *m, float *v, int64
 int zero_gather_write(const float *master, int64_t shard_len, const zero_chunk *d_chunks,
                       int64_t n_chunks, hipStream_t stream)
 {
-    if ((!master && shard_len > 0) || shard_len < 0 || n_chunks < 0 || n_chunks > INT32_MAX ||
+    if ((!master && shard_len > 0) || bad_len(shard_len) || n_chunks < 0 || n_chunks > INT32_MAX ||
         (n_chunks > 0 && !d_chunks))
         return ZERO_ERR_INVALID;
     if (!aligned16(master) || !aligned16(d_chunks))
@@ -514,7 +518,7 @@ int zero_gather_write(const float *master, int64_t shard_len, const zero_chunk *
 
 int zero_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream)
 {
-    if (((!src || !dst) && bytes > 0) || bytes < 0)
+    if (((!src || !dst) && bytes > 0) || bad_len(bytes))
         return ZERO_ERR_INVALID;
     if (!aligned16(src) || !aligned16(dst))
         return ZERO_ERR_MISALIGNED;
@@ -529,7 +533,7 @@ int zero_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t strea
 
 int zero_probe_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t magic, hipStream_t stream)
 {
-    if (((!src || !sink) && bytes > 0) || bytes < 0)
+    if (((!src || !sink) && bytes > 0) || bad_len(bytes))
         return ZERO_ERR_INVALID;
     if (!aligned16(src) || ((uintptr_t)sink & 3u) != 0)
         return ZERO_ERR_MISALIGNED;
@@ -542,7 +546,7 @@ int zero_probe_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t mag
 
 int zero_probe_write(void *dst, int64_t bytes, uint32_t value, hipStream_t stream)
 {
-    if ((!dst && bytes > 0) || bytes < 0)
+    if ((!dst && bytes > 0) || bad_len(bytes))
         return ZERO_ERR_INVALID;
     if (!aligned16(dst))
         return ZERO_ERR_MISALIGNED;

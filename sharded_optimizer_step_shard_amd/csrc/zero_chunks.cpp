@@ -24,7 +24,8 @@ int zero_build_chunks(const int64_t *numels, int n_tensors, int n_ranks, int ran
         return ZERO_ERR_INVALID;
     int64_t total = 0;
     for (int t = 0; t < n_tensors; ++t) {
-        if (numels[t] < 0 || (tensor_dst && numels[t] > 0 && !tensor_dst[t]))
+        if (numels[t] < 0 || numels[t] > ZERO_MAX_LEN - total ||
+            (tensor_dst && numels[t] > 0 && !tensor_dst[t]))
             return ZERO_ERR_INVALID;
         total += numels[t];
     }

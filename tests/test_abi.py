@@ -188,6 +188,37 @@ def test_unfused_argument_errors(zs):
     assert zs.raw_call("zero_probe_write", a, 64, 0, None) == zs.ZERO_ERR_NOT_DEVICE
 
 
+def test_lengths_above_the_limit_are_invalid(zs):
+    """Counts above ZERO_MAX_LEN (2^48) are INVALID in every entry point, so
+    no byte size formed from them can overflow int64; 2^48 itself passes the
+    length check and fails later (fake addresses: NOT_DEVICE or ALIAS)."""
+    big = zs.ZERO_MAX_LEN + 1
+    hp = zs.hparams(1)
+    a = BASE + (1 << 44)
+    assert step(zs, parts(4), 4, n=big) == zs.ZERO_ERR_INVALID
+    assert step(zs, parts(4), 4, n=1 << 62) == zs.ZERO_ERR_INVALID
+    assert step(zs, parts(4), 4, n=zs.ZERO_MAX_LEN) in (zs.ZERO_ERR_ALIAS, zs.ZERO_ERR_NOT_DEVICE)
+    assert kahan(zs, parts(4), 4, n=big) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_reduce_shard", parts(2), 2, 0, big, a, None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_adamw_shard", a, a + (1 << 40), a + (2 << 40), a + (3 << 40), big,
+                       ctypes.byref(hp), None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_gather_write", a, big, a + 4096, 1, None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_probe_copy", a, a + (1 << 50), big, None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_probe_read", a, big, a, 0, None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_probe_write", a, big, 0, None) == zs.ZERO_ERR_INVALID
+    # the chunk builder: a total above the limit, also when the sum would wrap int64
+    call = lambda *x: zs.raw_call("zero_build_chunks", *x)  # noqa: E731
+    for nm in ([zs.ZERO_MAX_LEN, 1], [(1 << 62), (1 << 62), (1 << 62)], [(1 << 63) - 1, 2]):
+        arr = np.array(nm, dtype=np.int64)
+        assert call(arr.ctypes.data, len(nm), 2, 0, None, BASE, 64, None, 0, None,
+                    None) == zs.ZERO_ERR_INVALID
+    arr = np.array([zs.ZERO_MAX_LEN - 5, 5], dtype=np.int64)
+    n = ctypes.c_int64(0)
+    assert call(arr.ctypes.data, 2, 1 << 20, 0, None, BASE, 1 << 24, None, 0, ctypes.byref(n),
+                None) == zs.ZERO_OK
+    assert n.value == (zs.ZERO_MAX_LEN >> 20) >> 24
+
+
 # ---------------------------------------------------------------- chunk table
 
 def expand(table):
