@@ -24,8 +24,10 @@
  * zero_adamw_shard and zero_gather_write do them one at a time and give the
  * same bits.  Variants of the fused pass: zero_shard_step_ex (two-level
  * reduce order, gradient accumulation), zero_shard_step_bf16_moments (fp32
- * master with bf16 m, v) and zero_shard_step_kahan (pure bf16 state with a
- * compensated update, no fp32 master).
+ * master with bf16 m, v), zero_shard_step_kahan (pure bf16 state with a
+ * compensated update, no fp32 master), zero_shard_step_buckets (one launch
+ * per gradient bucket) and zero_shard_step_scheduled (step constants read
+ * from device memory, for steps captured in a HIP graph).
  *
  * Arithmetic, fixed so that every result is reproducible bit for bit:
  *   - g: the partials are widened exactly to double and summed in double,
@@ -97,6 +99,18 @@ typedef struct zero_adamw_hparams {
     double weight_decay;
     int64_t step;
 } zero_adamw_hparams;
+
+/* The constants of one step, formed on the host in double from a
+ * zero_adamw_hparams (zero_make_step_consts); what the step kernels use.
+ * 80 bytes. */
+typedef struct zero_step_consts {
+    double b1, c1;     /* beta1, 1 - beta1 */
+    double b2, c2;     /* beta2, 1 - beta2 */
+    double bc1, bc2;   /* 1 - beta1^t, 1 - beta2^t */
+    double eps, lr;
+    double dec;        /* 1 - lr * weight_decay */
+    double wd;         /* weight_decay */
+} zero_step_consts;
 
 /* One chunk of a shard: shard elements [shard_off, shard_off + len), whose
  * bf16 parameters go to dst[0 .. len).  32 bytes.  Built on the host by
@@ -202,6 +216,51 @@ int zero_shard_step_buckets(const void *const *partials, int n_ranks, int gdt,
                             const int64_t *first, const int64_t *count, int n_buckets,
                             const hipEvent_t *ready, const zero_adamw_hparams *hp,
                             hipStream_t stream);
+
+/*
+ * Step constants in device memory, for steps captured in a HIP graph.
+ * A captured launch replays its arguments, so zero_shard_step's `hp`
+ * would apply the same step t (the same bias corrections, the same lr) on
+ * every replay.  Here the host forms the constants of each step of a run
+ * in advance, with exactly the arithmetic of zero_shard_step, into a table
+ * the caller keeps in device memory; a device counter names the entry the
+ * next launch uses, so each replay applies the next step of the run.
+ *
+ * zero_make_step_consts (host only): out[i] = the constants of hps[i] for
+ * i < count (host arrays; one entry per step, so a learning-rate schedule
+ * is just a different lr per entry).  INVALID, with nothing written, if
+ * count < 0, a pointer is NULL while count > 0, or any hps[i] is invalid
+ * as for zero_shard_step.
+ */
+int zero_make_step_consts(const zero_adamw_hparams *hps, int64_t count, zero_step_consts *out);
+
+/*
+ * zero_shard_step with its constants read on the device when the kernel
+ * runs: consts[*index] (consts: device array of n_consts entries, 16-byte
+ * aligned; index: device int64, 8-byte aligned).  The result equals
+ * zero_shard_step with the hparams that entry was made from, bit for bit.
+ * If *index is outside [0, n_consts) when the kernel runs, nothing is
+ * changed.  The call only reads the index; zero_step_index_advance moves it
+ * on once the optimizer step is complete (after every bucket of it, when
+ * the step is issued per bucket over sub-tables).
+ * Errors as zero_shard_step; also INVALID for a NULL consts or index or
+ * n_consts outside [1, INT32_MAX], MISALIGNED for a misaligned consts or
+ * index, ALIAS when consts or the index overlaps master, m or v, and
+ * NOT_DEVICE when either lies outside a device allocation.
+ */
+int zero_shard_step_scheduled(const void *const *partials, int n_ranks, int gdt,
+                              float *master, float *m, float *v, int64_t shard_len,
+                              const zero_chunk *d_chunks, int64_t n_chunks,
+                              const zero_step_consts *consts, int64_t n_consts,
+                              const int64_t *index, hipStream_t stream);
+
+/*
+ * Enqueue *index += 1 on `stream` (device int64, 8-byte aligned), applied
+ * only if 0 <= *index < n_consts when it runs: the counter stops at
+ * n_consts, past the last entry.  INVALID for a NULL index or
+ * n_consts < 1; MISALIGNED; NOT_DEVICE; HIP.
+ */
+int zero_step_index_advance(int64_t *index, int64_t n_consts, hipStream_t stream);
 
 /*
  * Extended reduce for data-parallel layouts beyond one flat group and for

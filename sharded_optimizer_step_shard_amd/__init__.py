@@ -48,6 +48,12 @@ def hparams(step: int, lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.99
     return HParams(lr, beta1, beta2, eps, weight_decay, step)
 
 
+# Mirrors `zero_step_consts` (80 bytes): the constants of one step.
+STEP_CONSTS_DTYPE = np.dtype([(f, "<f8") for f in
+                              ("b1", "c1", "b2", "c2", "bc1", "bc2", "eps", "lr", "dec", "wd")])
+assert STEP_CONSTS_DTYPE.itemsize == 80
+
+
 class ReduceSpec(ctypes.Structure):
     """Mirrors `zero_reduce_spec`."""
     _fields_ = [("group", ctypes.c_int32), ("micro_batches", ctypes.c_int32),
@@ -85,13 +91,18 @@ _lib.zero_gather_write.argtypes = [_vp, _i64, _vp, _i64, _vp]
 _lib.zero_probe_copy.argtypes = [_vp, _vp, _i64, _vp]
 _lib.zero_probe_read.argtypes = [_vp, _i64, _vp, ctypes.c_uint32, _vp]
 _lib.zero_probe_write.argtypes = [_vp, _i64, ctypes.c_uint32, _vp]
+_lib.zero_make_step_consts.argtypes = [_vp, _i64, _vp]
+_lib.zero_shard_step_scheduled.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
+                                           _i64, _vp, _vp]
+_lib.zero_step_index_advance.argtypes = [_vp, _i64, _vp]
 _lib.zero_strerror.argtypes = [_i32]
 _lib.zero_strerror.restype = ctypes.c_char_p
 for _f in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
            "zero_gather_write", "zero_probe_copy", "zero_probe_read", "zero_probe_write",
            "zero_version", "zero_shard_step_ex",
            "zero_accumulate_shard", "zero_shard_step_bf16_moments", "zero_shard_step_kahan",
-           "zero_shard_step_buckets"):
+           "zero_shard_step_buckets", "zero_make_step_consts", "zero_shard_step_scheduled",
+           "zero_step_index_advance"):
     getattr(_lib, _f).restype = _i32
 
 Ptr = Union[int, "torch.Tensor", None]  # noqa: F821
@@ -190,6 +201,34 @@ def zero_shard_step(partials: Sequence[Ptr], master: Ptr, m: Ptr, v: Ptr, shard_
     _check(_lib.zero_shard_step(_partial_array(partials), len(partials), gdt, _addr(master),
                                 _addr(m), _addr(v), shard_len, _addr(d_chunks), n_chunks,
                                 ctypes.byref(hp), _stream(stream)), "zero_shard_step")
+
+
+def zero_make_step_consts(hps: Sequence[HParams]) -> np.ndarray:
+    """Host table of step constants, one entry per hparams (STEP_CONSTS_DTYPE)."""
+    n = len(hps)
+    arr = (HParams * max(n, 1))(*hps)
+    out = np.zeros(n, dtype=STEP_CONSTS_DTYPE)
+    _check(_lib.zero_make_step_consts(ctypes.addressof(arr), n, out.ctypes.data if n else None),
+           "zero_make_step_consts")
+    return out
+
+
+def zero_shard_step_scheduled(partials: Sequence[Ptr], master: Ptr, m: Ptr, v: Ptr,
+                              shard_len: int, d_chunks: Ptr, n_chunks: int, consts: Ptr,
+                              n_consts: int, index: Ptr, gdt: Optional[int] = None,
+                              stream=None) -> None:
+    """Fused step whose constants are consts[*index], read on the device."""
+    gdt = _gdt_of(partials) if gdt is None else gdt
+    _check(_lib.zero_shard_step_scheduled(_partial_array(partials), len(partials), gdt,
+                                          _addr(master), _addr(m), _addr(v), shard_len,
+                                          _addr(d_chunks), n_chunks, _addr(consts), n_consts,
+                                          _addr(index), _stream(stream)),
+           "zero_shard_step_scheduled")
+
+
+def zero_step_index_advance(index: Ptr, n_consts: int, stream=None) -> None:
+    _check(_lib.zero_step_index_advance(_addr(index), n_consts, _stream(stream)),
+           "zero_step_index_advance")
 
 
 def zero_shard_step_buckets(partials: Sequence[Ptr], master: Ptr, m: Ptr, v: Ptr, shard_len: int,

@@ -137,7 +137,7 @@ bool in_device_alloc(const void *p, int64_t bytes)
 
 extern "C" {
 
-int zero_version(void) { return (1 << 16) | 6; }
+int zero_version(void) { return (1 << 16) | 7; }
 
 const char *zero_strerror(int code)
 {
@@ -158,12 +158,21 @@ const char *zero_strerror(int code)
 
 namespace zs {
 
+// Where the scheduled step finds its constants (device table and index).
+struct Schedule {
+    const zero_step_consts *consts;
+    int64_t n;
+    const int64_t *index;
+};
+
 // The checks of the 16-byte fused step, in the header's order, and its
-// kernel arguments.  Returns ZERO_OK with *empty set when there is nothing
-// to launch.
+// kernel arguments.  The constants come from hp, or, with sched given, from
+// a device table the scheduled step reads (hp is then unused).  Returns
+// ZERO_OK with *empty set when there is nothing to launch.
 static int prepare_step(const void *const *partials, int n_ranks, int gdt, float *master,
                         float *m, float *v, int64_t shard_len, const zero_chunk *d_chunks,
-                        int64_t n_chunks, const zero_adamw_hparams *hp, StepArgs &a, bool *empty)
+                        int64_t n_chunks, const zero_adamw_hparams *hp, StepArgs &a, bool *empty,
+                        const Schedule *sched = nullptr)
 {
     *empty = true;
     int rc = check_partials(partials, n_ranks, shard_len, a.parts);
@@ -171,10 +180,15 @@ static int prepare_step(const void *const *partials, int n_ranks, int gdt, float
         return rc;
     if (((!master || !m || !v) && shard_len > 0) || bad_len(shard_len) || n_chunks < 0 ||
         n_chunks > INT32_MAX ||
-        (n_chunks > 0 && !d_chunks) || !valid_hparams(hp))
+        (n_chunks > 0 && !d_chunks) || (!sched && !valid_hparams(hp)))
+        return ZERO_ERR_INVALID;
+    if (sched && (sched->n < 0 || sched->n > INT32_MAX ||
+                  (shard_len > 0 && (!sched->consts || !sched->index || sched->n < 1))))
         return ZERO_ERR_INVALID;
     if (!partials_aligned(a.parts, n_ranks) || !aligned16(master) || !aligned16(m) ||
         !aligned16(v) || !aligned16(d_chunks))
+        return ZERO_ERR_MISALIGNED;
+    if (sched && (!aligned16(sched->consts) || ((uintptr_t)sched->index & 7u) != 0))
         return ZERO_ERR_MISALIGNED;
     if (!valid_dtype(gdt))
         return ZERO_ERR_UNSUPPORTED;
@@ -185,6 +199,13 @@ static int prepare_step(const void *const *partials, int n_ranks, int gdt, float
         if (overlaps(partials[k], gb, master, sb) || overlaps(partials[k], gb, m, sb) ||
             overlaps(partials[k], gb, v, sb))
             return ZERO_ERR_ALIAS;
+    const int64_t cb = sched ? sched->n * (int64_t)sizeof(zero_step_consts) : 0;
+    if (sched && shard_len > 0) {
+        const void *outs[3] = {master, m, v};
+        for (const void *o : outs)
+            if (overlaps(sched->consts, cb, o, sb) || overlaps(sched->index, 8, o, sb))
+                return ZERO_ERR_ALIAS;
+    }
     if (n_chunks == 0 || shard_len == 0)
         return ZERO_OK;
     for (int k = 0; k < n_ranks; ++k)
@@ -193,8 +214,16 @@ static int prepare_step(const void *const *partials, int n_ranks, int gdt, float
     if (!in_device_alloc(master, sb) || !in_device_alloc(m, sb) || !in_device_alloc(v, sb) ||
         !in_device_alloc(d_chunks, n_chunks * (int64_t)sizeof(zero_chunk)))
         return ZERO_ERR_NOT_DEVICE;
+    if (sched && (!in_device_alloc(sched->consts, cb) || !in_device_alloc(sched->index, 8)))
+        return ZERO_ERR_NOT_DEVICE;
     a.red = make_reduce(n_ranks);
-    a.k = make_scalars(hp);
+    if (sched) {
+        a.sched = sched->consts;
+        a.n_sched = sched->n;
+        a.sched_index = sched->index;
+    } else {
+        a.k = make_scalars(hp);
+    }
     a.master = master;
     a.m = m;
     a.v = v;
@@ -268,6 +297,47 @@ int zero_shard_step_buckets(const void *const *partials, int n_ranks, int gdt,
             return rc;
     }
     return ZERO_OK;
+}
+
+int zero_make_step_consts(const zero_adamw_hparams *hps, int64_t count, zero_step_consts *out)
+{
+    if (count < 0 || count > INT32_MAX || (count > 0 && (!hps || !out)))
+        return ZERO_ERR_INVALID;
+    for (int64_t i = 0; i < count; ++i)
+        if (!valid_hparams(hps + i))
+            return ZERO_ERR_INVALID;
+    for (int64_t i = 0; i < count; ++i) {
+        const StepScalars k = make_scalars(hps + i);
+        memcpy(out + i, &k, sizeof(k));
+    }
+    return ZERO_OK;
+}
+
+int zero_shard_step_scheduled(const void *const *partials, int n_ranks, int gdt,
+                              float *master, float *m, float *v, int64_t shard_len,
+                              const zero_chunk *d_chunks, int64_t n_chunks,
+                              const zero_step_consts *consts, int64_t n_consts,
+                              const int64_t *index, hipStream_t stream)
+{
+    StepArgs a{};
+    bool empty;
+    const Schedule sched{consts, n_consts, index};
+    int rc = prepare_step(partials, n_ranks, gdt, master, m, v, shard_len, d_chunks, n_chunks,
+                          nullptr, a, &empty, &sched);
+    if (rc || empty)
+        return rc;
+    return hip_status(launch_step_sched(a, (zero_dtype)gdt, stream));
+}
+
+int zero_step_index_advance(int64_t *index, int64_t n_consts, hipStream_t stream)
+{
+    if (!index || n_consts < 1)
+        return ZERO_ERR_INVALID;
+    if (((uintptr_t)index & 7u) != 0)
+        return ZERO_ERR_MISALIGNED;
+    if (!in_device_alloc(index, 8))
+        return ZERO_ERR_NOT_DEVICE;
+    return hip_status(launch_index_advance(index, n_consts, stream));
 }
 
 int zero_shard_step_ex(const void *const *partials, int n_ranks, int gdt,

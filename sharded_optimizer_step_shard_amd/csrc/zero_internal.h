@@ -2,6 +2,7 @@
 // (zero_kernels.hip).  Not installed; the public ABI is include/zero_shard.h.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -19,6 +20,9 @@ struct StepScalars {
     double dec;        // 1 - lr * weight_decay
     double wd;         // weight_decay
 };
+static_assert(sizeof(StepScalars) == sizeof(zero_step_consts), "step constants layout");
+static_assert(offsetof(StepScalars, bc1) == offsetof(zero_step_consts, bc1), "step constants layout");
+static_assert(offsetof(StepScalars, wd) == offsetof(zero_step_consts, wd), "step constants layout");
 
 // Reduction constants: divide by the count (N, or N * micro-batches), or
 // multiply by its inverse when the count is a power of two (exact scaling,
@@ -46,6 +50,9 @@ struct StepArgs {
     int64_t shard_len;
     const float *acc;   // extended step: earlier micro-batches' sum, or null
     uint16_t *comp;     // pure-bf16 step: Kahan compensation (bf16), or null
+    const zero_step_consts *sched;   // scheduled step: constants table, its
+    const int64_t *sched_index;      // entry index and entry count
+    int64_t n_sched;
 };
 
 struct ReduceArgs {
@@ -78,6 +85,8 @@ struct GatherArgs {
 };
 
 hipError_t launch_step(const StepArgs &a, zero_dtype gdt, hipStream_t s);
+hipError_t launch_step_sched(const StepArgs &a, zero_dtype gdt, hipStream_t s);
+hipError_t launch_index_advance(int64_t *index, int64_t n, hipStream_t s);
 hipError_t launch_step_ex(const StepArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_step_m16(const StepArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_step_kahan(const StepArgs &a, zero_dtype gdt, hipStream_t s);

@@ -146,6 +146,7 @@ __device__ __forceinline__ T ld(const T *p) { return *p; }
 // (uniform) descriptor instead of one vector load per lane.
 typedef __attribute__((address_space(4))) const int64_t const_i64;
 typedef __attribute__((address_space(4))) const int32_t const_i32;
+typedef __attribute__((address_space(4))) const double const_f64;
 
 __device__ __forceinline__ zero_chunk chunk_at(const zero_chunk *table, int64_t ci)
 {
@@ -430,7 +431,8 @@ constexpr int kStepBatch = 8;
 // EXT: the extended reduce of zero_shard_step_ex (two-level order, optional
 // accumulator of earlier micro-batches, divisor N * micro-batches).
 template <zero_dtype G, int NC, bool EXT, int KC>
-__device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &c)
+__device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &c,
+                                           const StepScalars &k)
 {
     constexpr int VEC = Grad<G>::VEC;
     if (c.len <= 0 || c.shard_off < 0 || c.shard_off > a.shard_len - c.len)
@@ -470,7 +472,7 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
 #pragma unroll
             for (int j = 0; j < VEC; ++j) {
                 float gj = finish_reduce<EXT ? 0 : NC>(s[j], a.red);
-                adamw(gj, th[j], m[j], v[j], a.k);
+                adamw(gj, th[j], m[j], v[j], k);
                 h[j] = to_bf16(th[j]);
             }
             th.store(a.master + i0);
@@ -492,7 +494,7 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
                     gj = finish_reduce<NC>(elem_sum<G>(a.parts, n, i), a.red);
                 }
                 float th = a.master[i], m = a.m[i], v = a.v[i];
-                adamw(gj, th, m, v, a.k);
+                adamw(gj, th, m, v, k);
                 a.master[i] = th;
                 a.m[i] = m;
                 a.v[i] = v;
@@ -662,7 +664,37 @@ __global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, 1
 void shard_step_kernel(StepArgs a)
 {
     for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
-        step_chunk<G, NC, EXT, KC>(a, chunk_at(a.chunks, ci));
+        step_chunk<G, NC, EXT, KC>(a, chunk_at(a.chunks, ci), a.k);
+}
+
+// The 16-byte step with its constants in device memory: entry *a.sched_index
+// of the table a.sched (formed on the host, as the launch-argument constants
+// are).  A graph that captures this launch applies whichever step the index
+// names when it replays.  An index outside the table leaves everything
+// untouched.
+template <zero_dtype G, int NC>
+__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void shard_step_sched_kernel(StepArgs a)
+{
+    const int64_t t = *(const_i64 *)a.sched_index;
+    if (t < 0 || t >= a.n_sched)
+        return;
+    const const_f64 *e = (const const_f64 *)(a.sched + t);
+    StepScalars k;
+    k.b1 = e[0]; k.c1 = e[1]; k.b2 = e[2]; k.c2 = e[3]; k.bc1 = e[4]; k.bc2 = e[5];
+    k.eps = e[6]; k.lr = e[7]; k.dec = e[8]; k.wd = e[9];
+    for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
+        step_chunk<G, NC, false, -1>(a, chunk_at(a.chunks, ci), k);
+}
+
+// *index += 1 when 0 <= *index < n (one lane, a vector store).
+__global__ __launch_bounds__(64) void step_index_advance_kernel(int64_t *index, int64_t n)
+{
+    if (threadIdx.x == 0) {
+        const int64_t t = index[0];
+        if (t >= 0 && t < n)
+            index[0] = t + 1;
+    }
 }
 
 // ---------------------------------------------------------------- unfused
@@ -839,6 +871,35 @@ hipError_t launch_step(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 {
     return gdt == ZERO_BF16 ? step_dispatch<ZERO_BF16, false>(a, s)
                             : step_dispatch<ZERO_FP32, false>(a, s);
+}
+
+template <zero_dtype G>
+static hipError_t step_sched_dispatch(const StepArgs &a, hipStream_t s)
+{
+    dim3 grid(chunk_grid(a.n_chunks)), block(kStepBlock);
+    switch (a.red.n_ranks) {
+    case 1: hipLaunchKernelGGL((shard_step_sched_kernel<G, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((shard_step_sched_kernel<G, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((shard_step_sched_kernel<G, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((shard_step_sched_kernel<G, 8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((shard_step_sched_kernel<G, 16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((shard_step_sched_kernel<G, 32>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((shard_step_sched_kernel<G, 64>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((shard_step_sched_kernel<G, 0>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_step_sched(const StepArgs &a, zero_dtype gdt, hipStream_t s)
+{
+    return gdt == ZERO_BF16 ? step_sched_dispatch<ZERO_BF16>(a, s)
+                            : step_sched_dispatch<ZERO_FP32>(a, s);
+}
+
+hipError_t launch_index_advance(int64_t *index, int64_t n, hipStream_t s)
+{
+    hipLaunchKernelGGL(step_index_advance_kernel, dim3(1), dim3(64), 0, s, index, n);
+    return hipGetLastError();
 }
 
 // The extended step picks its fold at launch: groups of 1 or of all N ranks

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(zs):
 
 
 def test_version_and_strerror(zs):
-    assert zs.zero_version() == (1, 6)
+    assert zs.zero_version() == (1, 7)
     for code in range(8):
         assert zs.zero_strerror(code) and zs.zero_strerror(code) != "unknown error code"
     assert zs.zero_strerror(99) == "unknown error code"
@@ -373,3 +373,67 @@ def test_bucket_step_argument_errors(zs):
     assert buckets(zs, [], [], n_buckets=2) == E.ZERO_ERR_INVALID     # null arrays
     assert buckets(zs, [], [], n_buckets=-1) == E.ZERO_ERR_INVALID
     assert buckets(zs, [], [], n_buckets=0) == E.ZERO_ERR_NOT_DEVICE   # checks still run
+
+
+# ------------------------------------------------------- scheduled constants
+
+def test_step_consts_are_the_host_constants(zs):
+    """zero_make_step_consts forms each entry in double exactly as the
+    launch-argument path does: 1 - beta, 1 - beta^t with the C library's
+    pow (Python's float ** calls it), 1 - lr*wd."""
+    hps = [zs.hparams(t, lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd)
+           for t, lr, b1, b2, eps, wd in ((1, 1e-3, 0.9, 0.999, 1e-8, 0.1),
+                                          (7, 3e-4, 0.95, 0.98, 1e-6, 0.0),
+                                          (1000, 2.5e-5, 0.0, 0.5, 1e-12, 0.05),
+                                          (123456, 1e-2, 0.99, 0.9999, 0.0, 1.0))]
+    c = zs.zero_make_step_consts(hps)
+    for e, h in zip(c, hps):
+        want = (h.beta1, 1.0 - h.beta1, h.beta2, 1.0 - h.beta2, 1.0 - h.beta1 ** h.step,
+                1.0 - h.beta2 ** h.step, h.eps, h.lr, 1.0 - h.lr * h.weight_decay, h.weight_decay)
+        got = tuple(float(e[f]) for f in zs.STEP_CONSTS_DTYPE.names)
+        assert np.array(got).view(np.uint64).tolist() == np.array(want).view(np.uint64).tolist()
+    assert len(zs.zero_make_step_consts([])) == 0
+
+
+def test_step_consts_errors_write_nothing(zs):
+    hps = (zs.HParams * 3)(zs.hparams(1), zs.hparams(0), zs.hparams(2))
+    out = np.full(3 * 10, 7.0)                       # room for three entries
+    rc = zs.raw_call("zero_make_step_consts", ctypes.addressof(hps), 3, out.ctypes.data)
+    assert rc == zs.ZERO_ERR_INVALID and np.all(out == 7.0)
+    assert zs.raw_call("zero_make_step_consts", None, 2, out.ctypes.data) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_make_step_consts", ctypes.addressof(hps), -1, None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_make_step_consts", None, 0, None) == zs.ZERO_OK
+
+
+def sched(zs, consts=BASE + (3 << 40), n_consts=4, index=BASE + (3 << 40) + (1 << 20), n=1000,
+          master=BASE + (1 << 40), gdt=0):
+    return zs.raw_call("zero_shard_step_scheduled", parts(4), 4, gdt, master,
+                       BASE + (1 << 40) + (1 << 32), BASE + (1 << 40) + (2 << 32), n,
+                       BASE + (1 << 41), 1, consts, n_consts, index, None)
+
+
+def test_scheduled_step_argument_errors(zs):
+    E = zs
+    assert sched(zs) == E.ZERO_ERR_NOT_DEVICE                       # all checks pass on fake addresses
+    assert sched(zs, consts=None) == E.ZERO_ERR_INVALID
+    assert sched(zs, index=None) == E.ZERO_ERR_INVALID
+    assert sched(zs, n_consts=0) == E.ZERO_ERR_INVALID
+    assert sched(zs, n_consts=-1) == E.ZERO_ERR_INVALID
+    assert sched(zs, n_consts=1 << 31) == E.ZERO_ERR_INVALID
+    assert sched(zs, consts=BASE + (3 << 40) + 8) == E.ZERO_ERR_MISALIGNED
+    assert sched(zs, index=BASE + (3 << 40) + (1 << 20) + 4) == E.ZERO_ERR_MISALIGNED
+    assert sched(zs, gdt=5) == E.ZERO_ERR_UNSUPPORTED
+    # the table or the index inside master: ALIAS
+    assert sched(zs, consts=BASE + (1 << 40) + 16) == E.ZERO_ERR_ALIAS
+    assert sched(zs, index=BASE + (1 << 40) + 3992) == E.ZERO_ERR_ALIAS
+    assert sched(zs, index=BASE + (1 << 40) + 4000) == E.ZERO_ERR_NOT_DEVICE   # just past it
+    # empty shard: nothing to do, NULL table and index accepted
+    assert sched(zs, consts=None, index=None, n_consts=0, n=0) == E.ZERO_OK
+
+
+def test_index_advance_argument_errors(zs):
+    a = BASE + (3 << 40)
+    assert zs.raw_call("zero_step_index_advance", None, 4, None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_step_index_advance", a, 0, None) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_step_index_advance", a + 4, 4, None) == zs.ZERO_ERR_MISALIGNED
+    assert zs.raw_call("zero_step_index_advance", a, 4, None) == zs.ZERO_ERR_NOT_DEVICE
