@@ -246,6 +246,27 @@ class Shard:
                                    micro_batches=self.micro_batches, acc=self.acc)
         self.step_t = t
 
+    def use_schedule(self, t0: int, count: int) -> None:
+        """Constants of steps t0 .. t0+count-1 in a device table, read by
+        zero_shard_step_scheduled at a device index that
+        zero_step_index_advance moves on after each step (so a captured
+        graph replays consecutive steps)."""
+        import torch
+        hps = [self.zs.hparams(t, **self.w.hparams()) for t in range(t0, t0 + count)]
+        host = self.zs.zero_make_step_consts(hps)
+        self.consts = torch.from_numpy(host.view(np.uint8)).to(self.dev)
+        self.n_consts = count
+        self.sched_index = torch.zeros(1, dtype=torch.int64, device=self.dev)
+
+    def step_scheduled(self, t: int) -> None:
+        """One step with the table's next constants (t is the table's, not
+        the argument's)."""
+        self.zs.zero_shard_step_scheduled(self.partials, self.master, self.m, self.v, self.n,
+                                          self.d_table, len(self.table), self.consts,
+                                          self.n_consts, self.sched_index)
+        self.zs.zero_step_index_advance(self.sched_index, self.n_consts)
+        self.step_t = t
+
     def set_buckets(self, bucket_params: int) -> list:
         """ZeRO-2 style buckets: split the chunk table into contiguous runs of
         about bucket_params shard elements (whole chunks).  Each bucket is then
@@ -674,6 +695,10 @@ def main() -> int:
     ap.add_argument("--bucket-call", default="one", choices=["one", "per-bucket"],
                     help="with --bucket-params: enqueue all buckets with one "
                          "zero_shard_step_buckets call, or call zero_shard_step per bucket")
+    ap.add_argument("--scheduled", action="store_true",
+                    help="take the step constants from a device table (zero_shard_step_"
+                         "scheduled + zero_step_index_advance): with --graph every replay "
+                         "is the next step")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step's launches in a HIP graph and time its replays "
                          "(the hyper-parameters, step t included, are fixed at capture; the "
@@ -736,6 +761,11 @@ def main() -> int:
         else:
             sh.use_kahan()
             step = sh.step_kahan
+    if args.scheduled:
+        if extended or args.bucket_params > 0 or args.state != "fp32":
+            raise SystemExit("--scheduled runs the plain fused step on the fp32 state only")
+        sh.use_schedule(t, args.warmup + args.steps + 1)
+        step = sh.step_scheduled
     if args.bucket_params > 0:
         sh.set_buckets(args.bucket_params)
         step = sh.step_bucketed if args.bucket_call == "one" else sh.step_bucketed_loop
@@ -794,7 +824,7 @@ def main() -> int:
     if extended and args.micro_batches > 1:
         bytes_launch += 4 * sh.n           # the accumulator read by the fused launch
     achieved = bytes_launch / (kernel_ms * 1e-3) / 1e9
-    kname = STATES[args.state][0]
+    kname = "shard_step_sched_kernel" if args.scheduled else STATES[args.state][0]
     kernel_key = f"{kname}<{w.gdt},{w.n_ranks}{',ext' if extended else ''}>/{w.name}"
     traffic = load_traffic(kernel_key) if launches == 1 else None
     out = {
@@ -819,6 +849,7 @@ def main() -> int:
                    "launches_per_step": launches,
                    "max_chunk": int(sh.table["len"].max()) if len(sh.table) else 0,
                    "graph_replay": bool(args.graph),
+                   "scheduled_constants": bool(args.scheduled),
                    "bucket_call": args.bucket_call if args.bucket_params > 0 else None,
                    "parallelism": "one data-parallel rank's ZeRO shard"},
         "hbm_gbs": achieved,
