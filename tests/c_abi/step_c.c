@@ -4,8 +4,16 @@
  * zero_shard_step_bf16_moments when asked) with hipMalloc'd buffers, and
  * writes the results to another binary file for comparison.
  *
+ * State 2 runs the fp32-moment step from a HIP graph instead: the step with
+ * its constants in a device table (zero_shard_step_scheduled) and the index
+ * advance are captured once on a stream, and the graph is launched
+ * GRAPH_STEPS + 1 times.  The table holds steps step .. step+GRAPH_STEPS-1,
+ * so the launches apply those steps in turn and the last one, past the end
+ * of the table, changes nothing; the final index is checked.
+ *
  * Input file (little endian):  int32 n_ranks, int32 n_tensors, int32 rank,
- *   int32 state (0 = fp32 moments, 1 = bf16 moments), int64 step,
+ *   int32 state (0 = fp32 moments, 1 = bf16 moments, 2 = fp32 moments from a
+ *   graph), int64 step,
  *   double lr, beta1, beta2, eps, weight_decay, int64 numels[n_tensors],
  *   then for shard length S: uint16 partials[n_ranks][S], float master[S],
  *   then m[S], v[S] as float (state 0) or uint16 (state 1).
@@ -19,6 +27,8 @@
 #include <hip/hip_runtime_api.h>
 
 #include "zero_shard.h"
+
+#define GRAPH_STEPS 4
 
 #define CHECK_HIP(x) do { hipError_t e_ = (x); if (e_ != hipSuccess) { \
     fprintf(stderr, "%s failed: %s\n", #x, hipGetErrorString(e_)); exit(2); } } while (0)
@@ -61,7 +71,7 @@ int main(int argc, char **argv)
     CHECK_ZS(zero_build_chunks(numels, n_tensors, n_ranks, rank, NULL, d_params + lo, 2048,
                                table, n_chunks, &n_chunks, &S));
 
-    size_t mom = state ? 2 : 4;
+    size_t mom = state == 1 ? 2 : 4;
     uint16_t *h_parts = malloc((size_t)n_ranks * n * 2);
     float *h_master = malloc((size_t)n * 4);
     void *h_m = malloc((size_t)n * mom), *h_v = malloc((size_t)n * mom);
@@ -92,12 +102,51 @@ int main(int argc, char **argv)
     CHECK_HIP(hipMemset(d_params, 0xFF, (size_t)total * 2));
 
     zero_adamw_hparams hp = {hpd[0], hpd[1], hpd[2], hpd[3], hpd[4], step};
-    if (state == 0)
+    if (state == 0) {
         CHECK_ZS(zero_shard_step(parts, n_ranks, ZERO_BF16, d_master, (float *)d_m, (float *)d_v,
                                  n, d_table, n_chunks, &hp, 0));
-    else
+    } else if (state == 1) {
         CHECK_ZS(zero_shard_step_bf16_moments(parts, n_ranks, ZERO_BF16, d_master, (uint16_t *)d_m,
                                               (uint16_t *)d_v, n, d_table, n_chunks, &hp, 0));
+    } else {
+        zero_adamw_hparams hps[GRAPH_STEPS];
+        zero_step_consts consts[GRAPH_STEPS];
+        for (int i = 0; i < GRAPH_STEPS; ++i) {
+            hps[i] = hp;
+            hps[i].step = step + i;
+        }
+        CHECK_ZS(zero_make_step_consts(hps, GRAPH_STEPS, consts));
+        zero_step_consts *d_consts = NULL;
+        int64_t *d_index = NULL, index = 0;
+        CHECK_HIP(hipMalloc((void **)&d_consts, sizeof consts));
+        CHECK_HIP(hipMalloc((void **)&d_index, sizeof index));
+        CHECK_HIP(hipMemcpy(d_consts, consts, sizeof consts, hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemcpy(d_index, &index, sizeof index, hipMemcpyHostToDevice));
+        hipStream_t stream;
+        hipGraph_t graph;
+        hipGraphExec_t exec;
+        CHECK_HIP(hipStreamCreate(&stream));
+        CHECK_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal));
+        CHECK_ZS(zero_shard_step_scheduled(parts, n_ranks, ZERO_BF16, d_master, (float *)d_m,
+                                           (float *)d_v, n, d_table, n_chunks, d_consts,
+                                           GRAPH_STEPS, d_index, stream));
+        CHECK_ZS(zero_step_index_advance(d_index, GRAPH_STEPS, stream));
+        CHECK_HIP(hipStreamEndCapture(stream, &graph));
+        CHECK_HIP(hipGraphInstantiate(&exec, graph, NULL, NULL, 0));
+        for (int r = 0; r <= GRAPH_STEPS; ++r)
+            CHECK_HIP(hipGraphLaunch(exec, stream));
+        CHECK_HIP(hipStreamSynchronize(stream));
+        CHECK_HIP(hipMemcpy(&index, d_index, sizeof index, hipMemcpyDeviceToHost));
+        if (index != GRAPH_STEPS) {
+            fprintf(stderr, "index %lld after the launches, want %d\n", (long long)index, GRAPH_STEPS);
+            return 5;
+        }
+        CHECK_HIP(hipGraphExecDestroy(exec));
+        CHECK_HIP(hipGraphDestroy(graph));
+        CHECK_HIP(hipStreamDestroy(stream));
+        CHECK_HIP(hipFree(d_consts));
+        CHECK_HIP(hipFree(d_index));
+    }
     CHECK_HIP(hipDeviceSynchronize());
 
     uint16_t *h_params = malloc((size_t)total * 2);

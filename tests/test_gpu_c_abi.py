@@ -1,7 +1,9 @@
 """The C ABI from a plain C program (tests/c_abi/step_c.c, built by
 __graft_entry__.build() with gcc against libzero_shard.so): no Python, no
 torch on the library side.  The program's results are compared with the
-oracle."""
+oracle.  State 2 captures the scheduled step in a HIP graph with the HIP C
+API and launches it once per step of its table (four steps, then one launch
+past the end that must change nothing)."""
 import os
 import subprocess
 
@@ -17,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 EXE = os.path.join(HERE, "c_abi", "step_c")
 
 
-@pytest.mark.parametrize("state", [0, 1])
+@pytest.mark.parametrize("state", [0, 1, 2])
 def test_plain_c_program_matches_oracle(tmp_path, state):
     if not os.path.exists(EXE):
         pytest.fail(f"{EXE} not built: run __graft_entry__.build()")
@@ -31,7 +33,7 @@ def test_plain_c_program_matches_oracle(tmp_path, state):
     parts = host_partials(w, t, idx)
     master = host_master(w, idx)
     rng = np.random.default_rng(5)
-    if state == 0:
+    if state in (0, 2):
         m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
         v = (rng.random(n) * 1e-8).astype(np.float32)
     else:
@@ -53,8 +55,8 @@ def test_plain_c_program_matches_oracle(tmp_path, state):
     r = subprocess.run([EXE, str(inp), str(out)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     raw = open(out, "rb").read()
-    mb = 4 if state == 0 else 2
-    mdt = np.float32 if state == 0 else np.uint16
+    mb = 2 if state == 1 else 4
+    mdt = np.uint16 if state == 1 else np.float32
     off = 0
     g_master = np.frombuffer(raw, np.float32, n, off); off += 4 * n
     g_m = np.frombuffer(raw, mdt, n, off); off += mb * n
@@ -62,6 +64,10 @@ def test_plain_c_program_matches_oracle(tmp_path, state):
     g_params = np.frombuffer(raw, np.uint16, sum(numels), off)
     if state == 0:
         want = oracle.shard_step(parts, master, m, v, oracle.hparams(t, **hp))
+    elif state == 2:
+        want = (master, m, v, None)
+        for tt in range(t, t + 4):              # the program's table: steps t .. t+3
+            want = oracle.shard_step(parts, *want[:3], oracle.hparams(tt, **hp))
     else:
         want = oracle.shard_step_bf16m(parts, master, m, v, oracle.hparams(t, **hp))
     assert_bitwise(g_master, want[0], "C program master")
