@@ -217,50 +217,6 @@ int zero_shard_step_buckets(const void *const *partials, int n_ranks, int gdt,
                             const hipEvent_t *ready, const zero_adamw_hparams *hp,
                             hipStream_t stream);
 
-/*
- * Step constants in device memory, for steps captured in a HIP graph.
- * A captured launch replays its arguments, so zero_shard_step's `hp`
- * would apply the same step t (the same bias corrections, the same lr) on
- * every replay.  Here the host forms the constants of each step of a run
- * in advance, with exactly the arithmetic of zero_shard_step, into a table
- * the caller keeps in device memory; a device counter names the entry the
- * next launch uses, so each replay applies the next step of the run.
- *
- * zero_make_step_consts (host only): out[i] = the constants of hps[i] for
- * i < count (host arrays; one entry per step, so a learning-rate schedule
- * is just a different lr per entry).  INVALID, with nothing written, if
- * count < 0, a pointer is NULL while count > 0, or any hps[i] is invalid
- * as for zero_shard_step.
- */
-int zero_make_step_consts(const zero_adamw_hparams *hps, int64_t count, zero_step_consts *out);
-
-/*
- * zero_shard_step with its constants read on the device when the kernel
- * runs: consts[*index] (consts: device array of n_consts entries, 16-byte
- * aligned; index: device int64, 8-byte aligned).  The result equals
- * zero_shard_step with the hparams that entry was made from, bit for bit.
- * If *index is outside [0, n_consts) when the kernel runs, nothing is
- * changed.  The call only reads the index; zero_step_index_advance moves it
- * on once the optimizer step is complete (after every bucket of it, when
- * the step is issued per bucket over sub-tables).
- * Errors as zero_shard_step; also INVALID for a NULL consts or index or
- * n_consts outside [1, INT32_MAX], MISALIGNED for a misaligned consts or
- * index, ALIAS when consts or the index overlaps master, m or v, and
- * NOT_DEVICE when either lies outside a device allocation.
- */
-int zero_shard_step_scheduled(const void *const *partials, int n_ranks, int gdt,
-                              float *master, float *m, float *v, int64_t shard_len,
-                              const zero_chunk *d_chunks, int64_t n_chunks,
-                              const zero_step_consts *consts, int64_t n_consts,
-                              const int64_t *index, hipStream_t stream);
-
-/*
- * Enqueue *index += 1 on `stream` (device int64, 8-byte aligned), applied
- * only if 0 <= *index < n_consts when it runs: the counter stops at
- * n_consts, past the last entry.  INVALID for a NULL index or
- * n_consts < 1; MISALIGNED; NOT_DEVICE; HIP.
- */
-int zero_step_index_advance(int64_t *index, int64_t n_consts, hipStream_t stream);
 
 /*
  * Extended reduce for data-parallel layouts beyond one flat group and for
@@ -345,6 +301,70 @@ int zero_shard_step_kahan(const void *const *partials, int n_ranks, int gdt,
                           uint16_t *comp, uint16_t *m, uint16_t *v, int64_t shard_len,
                           const zero_chunk *d_chunks, int64_t n_chunks,
                           const zero_adamw_hparams *hp, hipStream_t stream);
+
+/*
+ * Step constants in device memory, for steps captured in a HIP graph.
+ * A captured launch replays its arguments, so zero_shard_step's `hp`
+ * would apply the same step t (the same bias corrections, the same lr) on
+ * every replay.  Here the host forms the constants of each step of a run
+ * in advance, with exactly the arithmetic of zero_shard_step, into a table
+ * the caller keeps in device memory; a device counter names the entry the
+ * next launch uses, so each replay applies the next step of the run.
+ *
+ * zero_make_step_consts (host only): out[i] = the constants of hps[i] for
+ * i < count (host arrays; one entry per step, so a learning-rate schedule
+ * is just a different lr per entry).  INVALID, with nothing written, if
+ * count < 0, a pointer is NULL while count > 0, or any hps[i] is invalid
+ * as for zero_shard_step.
+ */
+int zero_make_step_consts(const zero_adamw_hparams *hps, int64_t count, zero_step_consts *out);
+
+/*
+ * zero_shard_step with its constants read on the device when the kernel
+ * runs: consts[*index] (consts: device array of n_consts entries, 16-byte
+ * aligned; index: device int64, 8-byte aligned).  The result equals
+ * zero_shard_step with the hparams that entry was made from, bit for bit.
+ * If *index is outside [0, n_consts) when the kernel runs, nothing is
+ * changed.  The call only reads the index; zero_step_index_advance moves it
+ * on once the optimizer step is complete (after every bucket of it, when
+ * the step is issued per bucket over sub-tables).
+ * Errors as zero_shard_step; also INVALID for a NULL consts or index or
+ * n_consts outside [1, INT32_MAX], MISALIGNED for a misaligned consts or
+ * index, ALIAS when consts or the index overlaps master, m or v, and
+ * NOT_DEVICE when either lies outside a device allocation.
+ */
+int zero_shard_step_scheduled(const void *const *partials, int n_ranks, int gdt,
+                              float *master, float *m, float *v, int64_t shard_len,
+                              const zero_chunk *d_chunks, int64_t n_chunks,
+                              const zero_step_consts *consts, int64_t n_consts,
+                              const int64_t *index, hipStream_t stream);
+
+/*
+ * The 12-byte and pure-bf16 steps with their constants read on the device,
+ * as zero_shard_step_scheduled does for the 16-byte step.  Arguments as
+ * zero_shard_step_bf16_moments and zero_shard_step_kahan, with consts,
+ * n_consts and index in place of hp; results equal theirs bit for bit;
+ * errors as zero_shard_step_scheduled.
+ */
+int zero_shard_step_bf16_moments_scheduled(const void *const *partials, int n_ranks, int gdt,
+                                           float *master, uint16_t *m, uint16_t *v,
+                                           int64_t shard_len, const zero_chunk *d_chunks,
+                                           int64_t n_chunks, const zero_step_consts *consts,
+                                           int64_t n_consts, const int64_t *index,
+                                           hipStream_t stream);
+int zero_shard_step_kahan_scheduled(const void *const *partials, int n_ranks, int gdt,
+                                    uint16_t *comp, uint16_t *m, uint16_t *v, int64_t shard_len,
+                                    const zero_chunk *d_chunks, int64_t n_chunks,
+                                    const zero_step_consts *consts, int64_t n_consts,
+                                    const int64_t *index, hipStream_t stream);
+
+/*
+ * Enqueue *index += 1 on `stream` (device int64, 8-byte aligned), applied
+ * only if 0 <= *index < n_consts when it runs: the counter stops at
+ * n_consts, past the last entry.  INVALID for a NULL index or
+ * n_consts < 1; MISALIGNED; NOT_DEVICE; HIP.
+ */
+int zero_step_index_advance(int64_t *index, int64_t n_consts, hipStream_t stream);
 
 /*
  * Reduce only: grad_out[i] = fp32((p_0[i] + ... + p_{N-1}[i]) / N),

@@ -94,6 +94,8 @@ _lib.zero_probe_write.argtypes = [_vp, _i64, ctypes.c_uint32, _vp]
 _lib.zero_make_step_consts.argtypes = [_vp, _i64, _vp]
 _lib.zero_shard_step_scheduled.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
                                            _i64, _vp, _vp]
+_lib.zero_shard_step_bf16_moments_scheduled.argtypes = _lib.zero_shard_step_scheduled.argtypes
+_lib.zero_shard_step_kahan_scheduled.argtypes = _lib.zero_shard_step_scheduled.argtypes
 _lib.zero_step_index_advance.argtypes = [_vp, _i64, _vp]
 _lib.zero_strerror.argtypes = [_i32]
 _lib.zero_strerror.restype = ctypes.c_char_p
@@ -102,7 +104,8 @@ for _f in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_ad
            "zero_version", "zero_shard_step_ex",
            "zero_accumulate_shard", "zero_shard_step_bf16_moments", "zero_shard_step_kahan",
            "zero_shard_step_buckets", "zero_make_step_consts", "zero_shard_step_scheduled",
-           "zero_step_index_advance"):
+           "zero_step_index_advance", "zero_shard_step_bf16_moments_scheduled",
+           "zero_shard_step_kahan_scheduled"):
     getattr(_lib, _f).restype = _i32
 
 Ptr = Union[int, "torch.Tensor", None]  # noqa: F821
@@ -224,6 +227,30 @@ def zero_shard_step_scheduled(partials: Sequence[Ptr], master: Ptr, m: Ptr, v: P
                                           _addr(d_chunks), n_chunks, _addr(consts), n_consts,
                                           _addr(index), _stream(stream)),
            "zero_shard_step_scheduled")
+
+
+def zero_shard_step_bf16_moments_scheduled(partials: Sequence[Ptr], master: Ptr, m: Ptr, v: Ptr,
+                                           shard_len: int, d_chunks: Ptr, n_chunks: int,
+                                           consts: Ptr, n_consts: int, index: Ptr,
+                                           gdt: Optional[int] = None, stream=None) -> None:
+    """12-byte-state step whose constants are consts[*index], read on the device."""
+    gdt = _gdt_of(partials) if gdt is None else gdt
+    _check(_lib.zero_shard_step_bf16_moments_scheduled(
+        _partial_array(partials), len(partials), gdt, _addr(master), _addr(m), _addr(v), shard_len,
+        _addr(d_chunks), n_chunks, _addr(consts), n_consts, _addr(index), _stream(stream)),
+        "zero_shard_step_bf16_moments_scheduled")
+
+
+def zero_shard_step_kahan_scheduled(partials: Sequence[Ptr], comp: Ptr, m: Ptr, v: Ptr,
+                                    shard_len: int, d_chunks: Ptr, n_chunks: int, consts: Ptr,
+                                    n_consts: int, index: Ptr, gdt: Optional[int] = None,
+                                    stream=None) -> None:
+    """Pure-bf16 step whose constants are consts[*index], read on the device."""
+    gdt = _gdt_of(partials) if gdt is None else gdt
+    _check(_lib.zero_shard_step_kahan_scheduled(
+        _partial_array(partials), len(partials), gdt, _addr(comp), _addr(m), _addr(v), shard_len,
+        _addr(d_chunks), n_chunks, _addr(consts), n_consts, _addr(index), _stream(stream)),
+        "zero_shard_step_kahan_scheduled")
 
 
 def zero_step_index_advance(index: Ptr, n_consts: int, stream=None) -> None:

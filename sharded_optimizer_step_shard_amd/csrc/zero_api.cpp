@@ -158,61 +158,73 @@ const char *zero_strerror(int code)
 
 namespace zs {
 
-// Where the scheduled step finds its constants (device table and index).
+// Where a scheduled step finds its constants (device table and index).
 struct Schedule {
     const zero_step_consts *consts;
     int64_t n;
     const int64_t *index;
 };
 
-// The checks of the 16-byte fused step, in the header's order, and its
-// kernel arguments.  The constants come from hp, or, with sched given, from
-// a device table the scheduled step reads (hp is then unused).  Returns
-// ZERO_OK with *empty set when there is nothing to launch.
-static int prepare_step(const void *const *partials, int n_ranks, int gdt, float *master,
-                        float *m, float *v, int64_t shard_len, const zero_chunk *d_chunks,
-                        int64_t n_chunks, const zero_adamw_hparams *hp, StepArgs &a, bool *empty,
-                        const Schedule *sched = nullptr)
+// The three arrays a fused step updates in place (master, m, v; or comp, m,
+// v) and their element sizes in bytes.
+struct StateArrays {
+    const void *p[3];
+    int64_t eb[3];
+};
+
+// The checks of a fused step, in the header's order, and the kernel
+// arguments they have vetted (the caller sets the state pointers).  The
+// constants come from hp, or, with sched given, from the device table the
+// scheduled kernels read (hp is then unused).  Returns ZERO_OK with *empty
+// set when there is nothing to launch.
+static int prepare_fused(const void *const *partials, int n_ranks, int gdt, const StateArrays &st,
+                         int64_t shard_len, const zero_chunk *d_chunks, int64_t n_chunks,
+                         const zero_adamw_hparams *hp, const Schedule *sched, StepArgs &a,
+                         bool *empty)
 {
     *empty = true;
     int rc = check_partials(partials, n_ranks, shard_len, a.parts);
     if (rc)
         return rc;
-    if (((!master || !m || !v) && shard_len > 0) || bad_len(shard_len) || n_chunks < 0 ||
-        n_chunks > INT32_MAX ||
-        (n_chunks > 0 && !d_chunks) || (!sched && !valid_hparams(hp)))
+    if (((!st.p[0] || !st.p[1] || !st.p[2]) && shard_len > 0) || bad_len(shard_len) ||
+        n_chunks < 0 || n_chunks > INT32_MAX || (n_chunks > 0 && !d_chunks) ||
+        (!sched && !valid_hparams(hp)))
         return ZERO_ERR_INVALID;
     if (sched && (sched->n < 0 || sched->n > INT32_MAX ||
                   (shard_len > 0 && (!sched->consts || !sched->index || sched->n < 1))))
         return ZERO_ERR_INVALID;
-    if (!partials_aligned(a.parts, n_ranks) || !aligned16(master) || !aligned16(m) ||
-        !aligned16(v) || !aligned16(d_chunks))
+    if (!partials_aligned(a.parts, n_ranks) || !aligned16(st.p[0]) || !aligned16(st.p[1]) ||
+        !aligned16(st.p[2]) || !aligned16(d_chunks))
         return ZERO_ERR_MISALIGNED;
     if (sched && (!aligned16(sched->consts) || ((uintptr_t)sched->index & 7u) != 0))
         return ZERO_ERR_MISALIGNED;
     if (!valid_dtype(gdt))
         return ZERO_ERR_UNSUPPORTED;
-    const int64_t sb = shard_len * 4, gb = shard_len * elem_bytes(gdt);
-    if (overlaps(master, sb, m, sb) || overlaps(master, sb, v, sb) || overlaps(m, sb, v, sb))
-        return ZERO_ERR_ALIAS;
-    for (int k = 0; k < n_ranks; ++k)
-        if (overlaps(partials[k], gb, master, sb) || overlaps(partials[k], gb, m, sb) ||
-            overlaps(partials[k], gb, v, sb))
-            return ZERO_ERR_ALIAS;
-    const int64_t cb = sched ? sched->n * (int64_t)sizeof(zero_step_consts) : 0;
-    if (sched && shard_len > 0) {
-        const void *outs[3] = {master, m, v};
-        for (const void *o : outs)
-            if (overlaps(sched->consts, cb, o, sb) || overlaps(sched->index, 8, o, sb))
+    const int64_t gb = shard_len * elem_bytes(gdt);
+    const int64_t sb[3] = {shard_len * st.eb[0], shard_len * st.eb[1], shard_len * st.eb[2]};
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(st.p[i], sb[i], st.p[j], sb[j]))
                 return ZERO_ERR_ALIAS;
-    }
+    for (int k = 0; k < n_ranks; ++k)
+        for (int i = 0; i < 3; ++i)
+            if (overlaps(partials[k], gb, st.p[i], sb[i]))
+                return ZERO_ERR_ALIAS;
+    const int64_t cb = sched ? sched->n * (int64_t)sizeof(zero_step_consts) : 0;
+    if (sched && shard_len > 0)
+        for (int i = 0; i < 3; ++i)
+            if (overlaps(sched->consts, cb, st.p[i], sb[i]) ||
+                overlaps(sched->index, 8, st.p[i], sb[i]))
+                return ZERO_ERR_ALIAS;
     if (n_chunks == 0 || shard_len == 0)
         return ZERO_OK;
     for (int k = 0; k < n_ranks; ++k)
         if (!in_device_alloc(partials[k], gb))
             return ZERO_ERR_NOT_DEVICE;
-    if (!in_device_alloc(master, sb) || !in_device_alloc(m, sb) || !in_device_alloc(v, sb) ||
-        !in_device_alloc(d_chunks, n_chunks * (int64_t)sizeof(zero_chunk)))
+    for (int i = 0; i < 3; ++i)
+        if (!in_device_alloc(st.p[i], sb[i]))
+            return ZERO_ERR_NOT_DEVICE;
+    if (!in_device_alloc(d_chunks, n_chunks * (int64_t)sizeof(zero_chunk)))
         return ZERO_ERR_NOT_DEVICE;
     if (sched && (!in_device_alloc(sched->consts, cb) || !in_device_alloc(sched->index, 8)))
         return ZERO_ERR_NOT_DEVICE;
@@ -224,14 +236,62 @@ static int prepare_step(const void *const *partials, int n_ranks, int gdt, float
     } else {
         a.k = make_scalars(hp);
     }
-    a.master = master;
-    a.m = m;
-    a.v = v;
     a.chunks = d_chunks;
     a.n_chunks = n_chunks;
     a.shard_len = shard_len;
+    a.acc = nullptr;
     *empty = false;
     return ZERO_OK;
+}
+
+// The 16-byte state: fp32 master, m, v.
+static int prepare_step(const void *const *partials, int n_ranks, int gdt, float *master,
+                        float *m, float *v, int64_t shard_len, const zero_chunk *d_chunks,
+                        int64_t n_chunks, const zero_adamw_hparams *hp, StepArgs &a, bool *empty,
+                        const Schedule *sched = nullptr)
+{
+    const StateArrays st{{master, m, v}, {4, 4, 4}};
+    const int rc = prepare_fused(partials, n_ranks, gdt, st, shard_len, d_chunks, n_chunks, hp,
+                                 sched, a, empty);
+    a.master = master;
+    a.m = m;
+    a.v = v;
+    a.comp = nullptr;
+    return rc;
+}
+
+// The 12-byte state: fp32 master, bf16 m and v (read by the kernel as
+// 16-bit patterns through the float pointers).
+static int prepare_m16(const void *const *partials, int n_ranks, int gdt, float *master,
+                       uint16_t *m, uint16_t *v, int64_t shard_len, const zero_chunk *d_chunks,
+                       int64_t n_chunks, const zero_adamw_hparams *hp, StepArgs &a, bool *empty,
+                       const Schedule *sched = nullptr)
+{
+    const StateArrays st{{master, m, v}, {4, 2, 2}};
+    const int rc = prepare_fused(partials, n_ranks, gdt, st, shard_len, d_chunks, n_chunks, hp,
+                                 sched, a, empty);
+    a.master = master;
+    a.m = (float *)m;
+    a.v = (float *)v;
+    a.comp = nullptr;
+    return rc;
+}
+
+// The pure-bf16 state: compensation, m, v in bf16 (the parameters are the
+// chunk destinations).
+static int prepare_kahan(const void *const *partials, int n_ranks, int gdt, uint16_t *comp,
+                         uint16_t *m, uint16_t *v, int64_t shard_len, const zero_chunk *d_chunks,
+                         int64_t n_chunks, const zero_adamw_hparams *hp, StepArgs &a, bool *empty,
+                         const Schedule *sched = nullptr)
+{
+    const StateArrays st{{comp, m, v}, {2, 2, 2}};
+    const int rc = prepare_fused(partials, n_ranks, gdt, st, shard_len, d_chunks, n_chunks, hp,
+                                 sched, a, empty);
+    a.master = nullptr;
+    a.m = (float *)m;
+    a.v = (float *)v;
+    a.comp = comp;
+    return rc;
 }
 
 }  // namespace zs
@@ -326,7 +386,7 @@ int zero_shard_step_scheduled(const void *const *partials, int n_ranks, int gdt,
                           nullptr, a, &empty, &sched);
     if (rc || empty)
         return rc;
-    return hip_status(launch_step_sched(a, (zero_dtype)gdt, stream));
+    return hip_status(launch_step_sched(a, (zero_dtype)gdt, StateLayout::Fp32, stream));
 }
 
 int zero_step_index_advance(int64_t *index, int64_t n_consts, hipStream_t stream)
@@ -395,42 +455,11 @@ int zero_shard_step_bf16_moments(const void *const *partials, int n_ranks, int g
                                  const zero_adamw_hparams *hp, hipStream_t stream)
 {
     StepArgs a{};
-    int rc = check_partials(partials, n_ranks, shard_len, a.parts);
-    if (rc)
+    bool empty;
+    const int rc = prepare_m16(partials, n_ranks, gdt, master, m, v, shard_len, d_chunks,
+                               n_chunks, hp, a, &empty);
+    if (rc || empty)
         return rc;
-    if (((!master || !m || !v) && shard_len > 0) || bad_len(shard_len) || n_chunks < 0 ||
-        n_chunks > INT32_MAX || (n_chunks > 0 && !d_chunks) || !valid_hparams(hp))
-        return ZERO_ERR_INVALID;
-    if (!partials_aligned(a.parts, n_ranks) || !aligned16(master) || !aligned16(m) ||
-        !aligned16(v) || !aligned16(d_chunks))
-        return ZERO_ERR_MISALIGNED;
-    if (!valid_dtype(gdt))
-        return ZERO_ERR_UNSUPPORTED;
-    const int64_t fb = shard_len * 4, hb = shard_len * 2, gb = shard_len * elem_bytes(gdt);
-    if (overlaps(master, fb, m, hb) || overlaps(master, fb, v, hb) || overlaps(m, hb, v, hb))
-        return ZERO_ERR_ALIAS;
-    for (int k = 0; k < n_ranks; ++k)
-        if (overlaps(partials[k], gb, master, fb) || overlaps(partials[k], gb, m, hb) ||
-            overlaps(partials[k], gb, v, hb))
-            return ZERO_ERR_ALIAS;
-    if (n_chunks == 0 || shard_len == 0)
-        return ZERO_OK;
-    for (int k = 0; k < n_ranks; ++k)
-        if (!in_device_alloc(partials[k], gb))
-            return ZERO_ERR_NOT_DEVICE;
-    if (!in_device_alloc(master, fb) || !in_device_alloc(m, hb) || !in_device_alloc(v, hb) ||
-        !in_device_alloc(d_chunks, n_chunks * (int64_t)sizeof(zero_chunk)))
-        return ZERO_ERR_NOT_DEVICE;
-    a.red = make_reduce(n_ranks);
-    a.k = make_scalars(hp);
-    a.master = master;
-    a.m = (float *)m;        // the kernel reads these as 16-bit patterns
-    a.v = (float *)v;
-    a.chunks = d_chunks;
-    a.n_chunks = n_chunks;
-    a.shard_len = shard_len;
-    a.acc = nullptr;
-    a.comp = nullptr;
     return hip_status(launch_step_m16(a, (zero_dtype)gdt, stream));
 }
 
@@ -440,43 +469,45 @@ int zero_shard_step_kahan(const void *const *partials, int n_ranks, int gdt,
                           const zero_adamw_hparams *hp, hipStream_t stream)
 {
     StepArgs a{};
-    int rc = check_partials(partials, n_ranks, shard_len, a.parts);
-    if (rc)
+    bool empty;
+    const int rc = prepare_kahan(partials, n_ranks, gdt, comp, m, v, shard_len, d_chunks,
+                                 n_chunks, hp, a, &empty);
+    if (rc || empty)
         return rc;
-    if (((!comp || !m || !v) && shard_len > 0) || bad_len(shard_len) || n_chunks < 0 ||
-        n_chunks > INT32_MAX || (n_chunks > 0 && !d_chunks) || !valid_hparams(hp))
-        return ZERO_ERR_INVALID;
-    if (!partials_aligned(a.parts, n_ranks) || !aligned16(comp) || !aligned16(m) ||
-        !aligned16(v) || !aligned16(d_chunks))
-        return ZERO_ERR_MISALIGNED;
-    if (!valid_dtype(gdt))
-        return ZERO_ERR_UNSUPPORTED;
-    const int64_t hb = shard_len * 2, gb = shard_len * elem_bytes(gdt);
-    if (overlaps(comp, hb, m, hb) || overlaps(comp, hb, v, hb) || overlaps(m, hb, v, hb))
-        return ZERO_ERR_ALIAS;
-    for (int k = 0; k < n_ranks; ++k)
-        if (overlaps(partials[k], gb, comp, hb) || overlaps(partials[k], gb, m, hb) ||
-            overlaps(partials[k], gb, v, hb))
-            return ZERO_ERR_ALIAS;
-    if (n_chunks == 0 || shard_len == 0)
-        return ZERO_OK;
-    for (int k = 0; k < n_ranks; ++k)
-        if (!in_device_alloc(partials[k], gb))
-            return ZERO_ERR_NOT_DEVICE;
-    if (!in_device_alloc(comp, hb) || !in_device_alloc(m, hb) || !in_device_alloc(v, hb) ||
-        !in_device_alloc(d_chunks, n_chunks * (int64_t)sizeof(zero_chunk)))
-        return ZERO_ERR_NOT_DEVICE;
-    a.red = make_reduce(n_ranks);
-    a.k = make_scalars(hp);
-    a.master = nullptr;
-    a.m = (float *)m;        // the kernel reads these as 16-bit patterns
-    a.v = (float *)v;
-    a.comp = comp;
-    a.chunks = d_chunks;
-    a.n_chunks = n_chunks;
-    a.shard_len = shard_len;
-    a.acc = nullptr;
     return hip_status(launch_step_kahan(a, (zero_dtype)gdt, stream));
+}
+
+int zero_shard_step_bf16_moments_scheduled(const void *const *partials, int n_ranks, int gdt,
+                                           float *master, uint16_t *m, uint16_t *v,
+                                           int64_t shard_len, const zero_chunk *d_chunks,
+                                           int64_t n_chunks, const zero_step_consts *consts,
+                                           int64_t n_consts, const int64_t *index,
+                                           hipStream_t stream)
+{
+    StepArgs a{};
+    bool empty;
+    const Schedule sched{consts, n_consts, index};
+    const int rc = prepare_m16(partials, n_ranks, gdt, master, m, v, shard_len, d_chunks,
+                               n_chunks, nullptr, a, &empty, &sched);
+    if (rc || empty)
+        return rc;
+    return hip_status(launch_step_sched(a, (zero_dtype)gdt, StateLayout::Bf16Moments, stream));
+}
+
+int zero_shard_step_kahan_scheduled(const void *const *partials, int n_ranks, int gdt,
+                                    uint16_t *comp, uint16_t *m, uint16_t *v, int64_t shard_len,
+                                    const zero_chunk *d_chunks, int64_t n_chunks,
+                                    const zero_step_consts *consts, int64_t n_consts,
+                                    const int64_t *index, hipStream_t stream)
+{
+    StepArgs a{};
+    bool empty;
+    const Schedule sched{consts, n_consts, index};
+    const int rc = prepare_kahan(partials, n_ranks, gdt, comp, m, v, shard_len, d_chunks,
+                                 n_chunks, nullptr, a, &empty, &sched);
+    if (rc || empty)
+        return rc;
+    return hip_status(launch_step_sched(a, (zero_dtype)gdt, StateLayout::Kahan, stream));
 }
 
 int zero_accumulate_shard(const void *const *partials, int n_ranks, int gdt, int group,

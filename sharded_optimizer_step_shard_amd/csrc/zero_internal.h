@@ -85,7 +85,10 @@ struct GatherArgs {
 };
 
 hipError_t launch_step(const StepArgs &a, zero_dtype gdt, hipStream_t s);
-hipError_t launch_step_sched(const StepArgs &a, zero_dtype gdt, hipStream_t s);
+// The state layouts of the fused steps (which arrays master/m/v/comp are).
+enum class StateLayout { Fp32, Bf16Moments, Kahan };
+
+hipError_t launch_step_sched(const StepArgs &a, zero_dtype gdt, StateLayout layout, hipStream_t s);
 hipError_t launch_index_advance(int64_t *index, int64_t n, hipStream_t s);
 hipError_t launch_step_ex(const StepArgs &a, zero_dtype gdt, hipStream_t s);
 hipError_t launch_step_m16(const StepArgs &a, zero_dtype gdt, hipStream_t s);

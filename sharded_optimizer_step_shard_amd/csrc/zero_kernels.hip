@@ -523,7 +523,8 @@ constexpr int kM16Batch = kM16Waves<G, NC> == 2 ? 2 : kStepBatch;
 // as 16-bit patterns).  Same reduce and AdamW; the moments are read from
 // bf16 and rounded back to bf16 once, from double.
 template <zero_dtype G, int NC>
-__device__ __forceinline__ void step_chunk_m16(const StepArgs &a, const zero_chunk &c)
+__device__ __forceinline__ void step_chunk_m16(const StepArgs &a, const zero_chunk &c,
+                                               const StepScalars &k)
 {
     constexpr int VEC = Grad<G>::VEC;
     if (c.len <= 0 || c.shard_off < 0 || c.shard_off > a.shard_len - c.len)
@@ -549,7 +550,7 @@ __device__ __forceinline__ void step_chunk_m16(const StepArgs &a, const zero_chu
             for (int j = 0; j < VEC; ++j) {
                 double m1, v1;
                 adamw_d(finish_reduce<NC>(s[j], a.red), th[j], bf16_to_double(m.e[j]),
-                        bf16_to_double(v.e[j]), m1, v1, a.k);
+                        bf16_to_double(v.e[j]), m1, v1, k);
                 m.e[j] = bf16_from_double(m1);
                 v.e[j] = bf16_from_double(v1);
                 h[j] = to_bf16(th[j]);
@@ -566,7 +567,7 @@ __device__ __forceinline__ void step_chunk_m16(const StepArgs &a, const zero_chu
                 float th = a.master[i];
                 double m1, v1;
                 adamw_d(finish_reduce<NC>(elem_sum<G>(a.parts, n, i), a.red), th,
-                        bf16_to_double(m16[i]), bf16_to_double(v16[i]), m1, v1, a.k);
+                        bf16_to_double(m16[i]), bf16_to_double(v16[i]), m1, v1, k);
                 a.master[i] = th;
                 m16[i] = (uint16_t)bf16_from_double(m1);
                 v16[i] = (uint16_t)bf16_from_double(v1);
@@ -580,7 +581,8 @@ __device__ __forceinline__ void step_chunk_m16(const StepArgs &a, const zero_chu
 // the chunk's destination (the bf16 parameter is the only copy of the
 // weight), with bf16 compensation, m and v in shard order.
 template <zero_dtype G, int NC>
-__device__ __forceinline__ void step_chunk_kahan(const StepArgs &a, const zero_chunk &c)
+__device__ __forceinline__ void step_chunk_kahan(const StepArgs &a, const zero_chunk &c,
+                                                 const StepScalars &k)
 {
     constexpr int VEC = Grad<G>::VEC;
     if (c.len <= 0 || c.shard_off < 0 || c.shard_off > a.shard_len - c.len)
@@ -609,7 +611,7 @@ __device__ __forceinline__ void step_chunk_kahan(const StepArgs &a, const zero_c
             group_sum<G, NC>(s, a.parts, n, i0);
 #pragma unroll
             for (int j = 0; j < VEC; ++j)
-                kahan_elem(finish_reduce<NC>(s[j], a.red), th.e[j], cm.e[j], m.e[j], v.e[j], a.k);
+                kahan_elem(finish_reduce<NC>(s[j], a.red), th.e[j], cm.e[j], m.e[j], v.e[j], k);
             cm.store(c16 + i0);
             m.store(m16 + i0);
             v.store(v16 + i0);
@@ -620,7 +622,7 @@ __device__ __forceinline__ void step_chunk_kahan(const StepArgs &a, const zero_c
                 if (i < lo || i >= hi)
                     continue;
                 uint32_t th = d[j], cm = c16[i], m = m16[i], v = v16[i];
-                kahan_elem(finish_reduce<NC>(elem_sum<G>(a.parts, n, i), a.red), th, cm, m, v, a.k);
+                kahan_elem(finish_reduce<NC>(elem_sum<G>(a.parts, n, i), a.red), th, cm, m, v, k);
                 d[j] = (uint16_t)th;
                 c16[i] = (uint16_t)cm;
                 m16[i] = (uint16_t)m;
@@ -635,7 +637,7 @@ __global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, k
 void shard_step_kahan_kernel(StepArgs a)
 {
     for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
-        step_chunk_kahan<G, NC>(a, chunk_at(a.chunks, ci));
+        step_chunk_kahan<G, NC>(a, chunk_at(a.chunks, ci), a.k);
 }
 
 template <zero_dtype G, int NC>
@@ -643,7 +645,7 @@ __global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, k
 void shard_step_m16_kernel(StepArgs a)
 {
     for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
-        step_chunk_m16<G, NC>(a, chunk_at(a.chunks, ci));
+        step_chunk_m16<G, NC>(a, chunk_at(a.chunks, ci), a.k);
 }
 
 // In every chunk-table kernel a workgroup (one wave) takes chunks
@@ -667,13 +669,18 @@ void shard_step_kernel(StepArgs a)
         step_chunk<G, NC, EXT, KC>(a, chunk_at(a.chunks, ci), a.k);
 }
 
-// The 16-byte step with its constants in device memory: entry *a.sched_index
-// of the table a.sched (formed on the host, as the launch-argument constants
-// are).  A graph that captures this launch applies whichever step the index
-// names when it replays.  An index outside the table leaves everything
-// untouched.
-template <zero_dtype G, int NC>
-__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// The fused steps with their constants in device memory: entry
+// *a.sched_index of the table a.sched (formed on the host, as the
+// launch-argument constants are).  A graph that captures this launch applies
+// whichever step the index names when it replays.  An index outside the
+// table leaves everything untouched.  L: the state layout (0: fp32 master,
+// m, v; 1: fp32 master, bf16 m, v; 2: pure bf16 with compensation), each
+// with the occupancy of its launch-argument kernel.
+template <int L, zero_dtype G, int NC>
+constexpr int kSchedWaves = L == 0 ? 1 : (L == 1 ? kM16Waves<G, NC> : kKahanWaves);
+
+template <int L, zero_dtype G, int NC>
+__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, kSchedWaves<L, G, NC>)))
 void shard_step_sched_kernel(StepArgs a)
 {
     const int64_t t = *(const_i64 *)a.sched_index;
@@ -683,8 +690,14 @@ void shard_step_sched_kernel(StepArgs a)
     StepScalars k;
     k.b1 = e[0]; k.c1 = e[1]; k.b2 = e[2]; k.c2 = e[3]; k.bc1 = e[4]; k.bc2 = e[5];
     k.eps = e[6]; k.lr = e[7]; k.dec = e[8]; k.wd = e[9];
-    for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
-        step_chunk<G, NC, false, -1>(a, chunk_at(a.chunks, ci), k);
+    for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x) {
+        if constexpr (L == 0)
+            step_chunk<G, NC, false, -1>(a, chunk_at(a.chunks, ci), k);
+        else if constexpr (L == 1)
+            step_chunk_m16<G, NC>(a, chunk_at(a.chunks, ci), k);
+        else
+            step_chunk_kahan<G, NC>(a, chunk_at(a.chunks, ci), k);
+    }
 }
 
 // *index += 1 when 0 <= *index < n (one lane, a vector store).
@@ -873,27 +886,38 @@ hipError_t launch_step(const StepArgs &a, zero_dtype gdt, hipStream_t s)
                             : step_dispatch<ZERO_FP32, false>(a, s);
 }
 
-template <zero_dtype G>
+template <int L, zero_dtype G>
 static hipError_t step_sched_dispatch(const StepArgs &a, hipStream_t s)
 {
     dim3 grid(chunk_grid(a.n_chunks)), block(kStepBlock);
     switch (a.red.n_ranks) {
-    case 1: hipLaunchKernelGGL((shard_step_sched_kernel<G, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((shard_step_sched_kernel<G, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((shard_step_sched_kernel<G, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((shard_step_sched_kernel<G, 8>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((shard_step_sched_kernel<G, 16>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((shard_step_sched_kernel<G, 32>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((shard_step_sched_kernel<G, 64>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((shard_step_sched_kernel<G, 0>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 32>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 64>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 0>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_step_sched(const StepArgs &a, zero_dtype gdt, hipStream_t s)
+template <int L>
+static hipError_t step_sched_layout(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 {
-    return gdt == ZERO_BF16 ? step_sched_dispatch<ZERO_BF16>(a, s)
-                            : step_sched_dispatch<ZERO_FP32>(a, s);
+    return gdt == ZERO_BF16 ? step_sched_dispatch<L, ZERO_BF16>(a, s)
+                            : step_sched_dispatch<L, ZERO_FP32>(a, s);
+}
+
+hipError_t launch_step_sched(const StepArgs &a, zero_dtype gdt, StateLayout layout, hipStream_t s)
+{
+    switch (layout) {
+    case StateLayout::Fp32: return step_sched_layout<0>(a, gdt, s);
+    case StateLayout::Bf16Moments: return step_sched_layout<1>(a, gdt, s);
+    case StateLayout::Kahan: return step_sched_layout<2>(a, gdt, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_index_advance(int64_t *index, int64_t n, hipStream_t s)

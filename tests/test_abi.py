@@ -437,3 +437,24 @@ def test_index_advance_argument_errors(zs):
     assert zs.raw_call("zero_step_index_advance", a, 0, None) == zs.ZERO_ERR_INVALID
     assert zs.raw_call("zero_step_index_advance", a + 4, 4, None) == zs.ZERO_ERR_MISALIGNED
     assert zs.raw_call("zero_step_index_advance", a, 4, None) == zs.ZERO_ERR_NOT_DEVICE
+
+
+def test_scheduled_layouts_share_the_checks(zs):
+    """The 12-byte and pure-bf16 scheduled forms run the same checks, with
+    their own element sizes: bf16 m and v are 2 bytes per element."""
+    m, v = BASE + (1 << 40) + (1 << 32), BASE + (1 << 40) + (2 << 32)
+    consts, index = BASE + (3 << 40), BASE + (3 << 40) + (1 << 20)
+    for name, first in (("zero_shard_step_bf16_moments_scheduled", BASE + (1 << 40)),
+                        ("zero_shard_step_kahan_scheduled", BASE + (1 << 40))):
+        call = lambda **kw: zs.raw_call(name, parts(4), 4, kw.get("gdt", 0), first,  # noqa: E731
+                                        m, kw.get("v", v), 1000, BASE + (1 << 41), 1,
+                                        kw.get("consts", consts), kw.get("n_consts", 4),
+                                        kw.get("index", index), None)
+        assert call() == zs.ZERO_ERR_NOT_DEVICE
+        assert call(consts=None) == zs.ZERO_ERR_INVALID
+        assert call(n_consts=0) == zs.ZERO_ERR_INVALID
+        assert call(index=index + 4) == zs.ZERO_ERR_MISALIGNED
+        assert call(gdt=3) == zs.ZERO_ERR_UNSUPPORTED
+        assert call(v=m + 1984) == zs.ZERO_ERR_ALIAS              # bf16 m spans 2000 bytes
+        assert call(v=m + 2000) == zs.ZERO_ERR_NOT_DEVICE
+        assert call(index=m + 1992) == zs.ZERO_ERR_ALIAS

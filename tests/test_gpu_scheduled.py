@@ -1,12 +1,13 @@
-"""The fused step with its constants in device memory
-(zero_shard_step_scheduled, zero_step_index_advance).
+"""The fused steps with their constants in device memory
+(zero_shard_step_scheduled and its 12-byte and pure-bf16 forms,
+zero_step_index_advance).
 
 - Eager calls: entry i of the table gives the bits of zero_shard_step with
   the hparams entry i was made from; the call leaves the index as it is; an
   index outside the table changes nothing.
-- Graph capture: one step (the scheduled launch and the index advance) is
-  captured once and replayed six times with a learning-rate schedule in the
-  table.  The state carries over from replay to replay, as in training; the
+- Graph capture, for each state layout: one step (the scheduled launch and
+  the index advance) is captured once and replayed six times with a
+  learning-rate schedule in the table.  The state carries over from replay to replay, as in training; the
   partials are refilled eagerly between replays.  After every replay the
   state equals the oracle's run of that many steps with the scheduled
   hparams, and the index has moved on by one.  Replays past the end of the
@@ -114,8 +115,9 @@ def test_index_advance_stops_at_the_end(zs):
     assert int(index.item()) == -3
 
 
-def test_graph_replays_follow_the_schedule(zs):
-    say("case: scheduled step captured in a graph, six replays with a learning-rate schedule")
+@pytest.mark.parametrize("layout", ["fp32", "bf16-moments", "bf16-kahan"])
+def test_graph_replays_follow_the_schedule(zs, layout):
+    say(f"case: scheduled {layout} step captured in a graph, six replays with a learning-rate schedule")
     n_steps = 6
     w, rank, n, idx, slot, d_table, nc = setup(zs)
     sch = schedule(n_steps)
@@ -125,10 +127,21 @@ def test_graph_replays_follow_the_schedule(zs):
     parts_h = {t: host_partials(w, t, idx) for t in range(1, n_steps + 1)}
     parts = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(w.n_ranks)]
     th0 = host_master(w, idx)
-    master, m, v = dev(th0), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    z16 = np.zeros(n, np.uint16)
+    if layout == "fp32":
+        state_h = (th0, np.zeros(n, np.float32), np.zeros(n, np.float32))
+        fn, oracle_step = zs.zero_shard_step_scheduled, oracle.shard_step
+    elif layout == "bf16-moments":
+        state_h = (th0, z16, z16)
+        fn, oracle_step = zs.zero_shard_step_bf16_moments_scheduled, oracle.shard_step_bf16m
+    else:
+        state_h = (oracle.bf16_round(th0), z16, z16, z16)
+        slot.copy_(dev(state_h[0]))
+        fn, oracle_step = zs.zero_shard_step_kahan_scheduled, oracle.shard_step_kahan
+    bufs = [dev(x) for x in (state_h if layout != "bf16-kahan" else state_h[1:])]
 
     def one_step():
-        zs.zero_shard_step_scheduled(parts, master, m, v, n, d_table, nc, consts, len(hps), index)
+        fn(parts, *bufs, n, d_table, nc, consts, len(hps), index)
         zs.zero_step_index_advance(index, len(hps))
 
     graph = torch.cuda.CUDAGraph()
@@ -141,25 +154,31 @@ def test_graph_replays_follow_the_schedule(zs):
     torch.cuda.synchronize()
     # capture only records: nothing ran
     assert int(index.item()) == 0
-    assert_bitwise(host(master), th0, "state untouched by the capture")
+    assert_bitwise(host(bufs[0]), state_h[0] if layout != "bf16-kahan" else state_h[1],
+                   "state untouched by the capture")
 
-    th, mm, vv = th0, np.zeros(n, np.float32), np.zeros(n, np.float32)
-    p = None
+    st = state_h
     for t in range(1, n_steps + 1):
         for d, h in zip(parts, parts_h[t]):        # eager work between replays
             d.copy_(dev(h))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        th, mm, vv, p = oracle.shard_step(parts_h[t], th, mm, vv, oracle.hparams(t, **sch[t - 1]))
-        for got, want, what in ((master, th, "master"), (m, mm, "m"), (v, vv, "v"), (slot, p, "param")):
-            assert_bitwise(host(got), want, f"replay {t} {what}")
+        out = oracle_step(parts_h[t], *st, oracle.hparams(t, **sch[t - 1]))
+        if layout == "bf16-kahan":
+            st = out
+            want = list(out[1:]) + [out[0]]        # comp, m, v, then the parameters
+        else:
+            st = out[:3]
+            want = list(out)                        # master, m, v, parameters
+        for k, (got, w_) in enumerate(zip(bufs + [slot], want)):
+            assert_bitwise(host(got), w_, f"{layout} replay {t} array {k}")
         assert int(index.item()) == t
     # past the end of the table: replays change nothing
-    before = [x.clone() for x in (master, m, v, slot)]
+    before = [x.clone() for x in bufs + [slot]]
     graph.replay()
     graph.replay()
     torch.cuda.synchronize()
-    for x, y in zip((master, m, v, slot), before):
+    for x, y in zip(bufs + [slot], before):
         assert torch.equal(x, y)
     assert int(index.item()) == n_steps
