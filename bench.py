@@ -261,9 +261,15 @@ class Shard:
     def step_scheduled(self, t: int) -> None:
         """One step with the table's next constants (t is the table's, not
         the argument's)."""
-        self.zs.zero_shard_step_scheduled(self.partials, self.master, self.m, self.v, self.n,
-                                          self.d_table, len(self.table), self.consts,
-                                          self.n_consts, self.sched_index)
+        state = getattr(self, "state", "fp32")
+        if state == "bf16-kahan":
+            fn, first = self.zs.zero_shard_step_kahan_scheduled, self.comp
+        elif state == "bf16-moments":
+            fn, first = self.zs.zero_shard_step_bf16_moments_scheduled, self.master
+        else:
+            fn, first = self.zs.zero_shard_step_scheduled, self.master
+        fn(self.partials, first, self.m, self.v, self.n, self.d_table, len(self.table),
+           self.consts, self.n_consts, self.sched_index)
         self.zs.zero_step_index_advance(self.sched_index, self.n_consts)
         self.step_t = t
 
@@ -762,8 +768,8 @@ def main() -> int:
             sh.use_kahan()
             step = sh.step_kahan
     if args.scheduled:
-        if extended or args.bucket_params > 0 or args.state != "fp32":
-            raise SystemExit("--scheduled runs the plain fused step on the fp32 state only")
+        if extended or args.bucket_params > 0:
+            raise SystemExit("--scheduled runs the plain fused step of each state layout")
         sh.use_schedule(t, args.warmup + args.steps + 1)
         step = sh.step_scheduled
     if args.bucket_params > 0:
