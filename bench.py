@@ -48,6 +48,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # description.
 STATES = {
     "fp32": ("shard_step_kernel", 12, 14, "fp32 master, m, v; bf16 parameter written"),
+    # the same step as three kernels: reduce (2N read, 4 written), AdamW (16
+    # read, 12 written), bf16 write (4 read, 2 written)
+    "unfused": ("reduce_kernel+adamw_kernel+gather_kernel", 20, 18,
+                "fp32 master, m, v; fp32 gradient shard between the phases"),
     "bf16-moments": ("shard_step_m16_kernel", 8, 10, "fp32 master, bf16 m, v; bf16 parameter written"),
     "bf16-kahan": ("shard_step_kahan_kernel", 8, 8,
                    "bf16 parameter (read and written in place), bf16 Kahan compensation, m, v"),
@@ -273,6 +277,20 @@ class Shard:
         self.zs.zero_step_index_advance(self.sched_index, self.n_consts)
         self.step_t = t
 
+    def use_unfused(self) -> None:
+        """The three phases as separate kernels (reduce into an fp32 gradient
+        shard, AdamW, bf16 write), for comparison with the fused step."""
+        import torch
+        self.grad = torch.empty(self.n, dtype=torch.float32, device=self.dev)
+        self.state = "unfused"
+
+    def step_unfused(self, t: int) -> None:
+        self.zs.zero_reduce_shard(self.partials, self.n, self.grad)
+        self.zs.zero_adamw_shard(self.grad, self.master, self.m, self.v, self.n,
+                                 self.zs.hparams(t, **self.w.hparams()))
+        self.zs.zero_gather_write(self.master, self.n, self.d_table, len(self.table))
+        self.step_t = t
+
     def set_buckets(self, bucket_params: int) -> list:
         """ZeRO-2 style buckets: split the chunk table into contiguous runs of
         about bucket_params shard elements (whole chunks).  Each bucket is then
@@ -383,7 +401,7 @@ def cpu_baseline(w: W.Workload, rank: int, t: int, target_s: float = 10.0,
         while elapsed < budget:
             hp = oracle.hparams(t + reps, **w.hparams())
             t0 = time.perf_counter()
-            if state == "fp32":
+            if state in ("fp32", "unfused"):
                 oracle.shard_step(sub, th, m, v, hp, in_place=True)
             elif state == "bf16-moments":
                 th, m16, v16, _ = oracle.shard_step_bf16m(sub, th, m16, v16, hp)
@@ -690,7 +708,8 @@ def main() -> int:
     ap.add_argument("--state", default="fp32", choices=sorted(STATES),
                     help="optimizer state: fp32 master, m, v (16 B/param ledger); fp32 "
                          "master with bf16 m, v (12 B/param ledger); or pure bf16 with a "
-                         "Kahan-compensated update (no master, 10 B/param)")
+                         "Kahan-compensated update (no master, 10 B/param).  'unfused' runs "
+                         "the 16 B/param step as three kernels (reduce, AdamW, bf16 write)")
     ap.add_argument("--group", type=int, default=0,
                     help="two-level reduce: ranks per group (hybrid sharding); 0 = flat")
     ap.add_argument("--micro-batches", type=int, default=1,
@@ -761,7 +780,12 @@ def main() -> int:
     if args.state != "fp32":
         if extended or args.bucket_params > 0:
             raise SystemExit(f"--state {args.state} runs the plain fused step only")
-        if args.state == "bf16-moments":
+        if args.state == "unfused":
+            if args.scheduled or args.graph:
+                raise SystemExit("--state unfused runs eagerly with launch-argument constants")
+            sh.use_unfused()
+            step = sh.step_unfused
+        elif args.state == "bf16-moments":
             sh.use_bf16_moments()
             step = sh.step_bf16_moments
         else:

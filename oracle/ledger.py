@@ -67,6 +67,22 @@ def shard_step_bytes_per_param(n_ranks: int, grad_bytes: int = 2, moment_bytes: 
     return n_ranks * grad_bytes + 2 * (s["master"] + 2 * moment_bytes) + s["param"]
 
 
+def unfused_step_bytes_per_param(n_ranks: int, grad_bytes: int = 2) -> int:
+    """HBM bytes per shard element when the three phases run as separate
+    passes with an fp32 gradient shard between them ("并行训练优化、MoE扩展与系统瓶颈",
+    2.2.4: reduce-scatter, then the optimizer step on the shard, then the
+    all-gather): the reduce reads N partials and writes the gradient; the
+    optimizer step reads the gradient and master, m, v and writes master, m,
+    v; the parameter write reads the master again and writes the 16-bit
+    parameter."""
+    s = STATE_ELEMENT_BYTES
+    g32 = 4
+    reduce_pass = n_ranks * grad_bytes + g32
+    adam_pass = g32 + 2 * (s["master"] + s["m"] + s["v"])
+    write_pass = s["master"] + s["param"]
+    return reduce_pass + adam_pass + write_pass
+
+
 def kahan_step_bytes_per_param(n_ranks: int, grad_bytes: int = 2) -> int:
     """HBM bytes of the fused pure-bf16 step per shard element: N gradient
     partials read; parameter, compensation, m, v (bf16 each) read and

@@ -97,12 +97,13 @@ def test_trace_summary_groups_by_kernel_and_grid(tmp_path):
 def test_bench_byte_model_matches_the_ledger(n_ranks, gdt):
     """The algorithmic bytes bench.py prices each state layout at are the
     oracle ledger's per-element step bytes (2N + 26, 2N + 18, 2N + 16 with
-    bf16 partials)."""
+    bf16 partials; 2N + 38 for the three phases run separately)."""
     from oracle import ledger
     gb = 2 if gdt == "bf16" else 4
     want = {"fp32": ledger.shard_step_bytes_per_param(n_ranks, gb, 4),
             "bf16-moments": ledger.shard_step_bytes_per_param(n_ranks, gb, 2),
-            "bf16-kahan": ledger.kahan_step_bytes_per_param(n_ranks, gb)}
+            "bf16-kahan": ledger.kahan_step_bytes_per_param(n_ranks, gb),
+            "unfused": ledger.unfused_step_bytes_per_param(n_ranks, gb)}
     assert set(want) == set(bench.STATES)
     for state, (_, rd, wr, _) in bench.STATES.items():
         assert n_ranks * gb + rd + wr == want[state], state

@@ -396,3 +396,7 @@ def test_shard_step_byte_model():
     for n in (1, 4, 8, 16, 32, 64):
         assert ledger.shard_step_bytes_per_param(n) == 2 * n + 26
         assert ledger.shard_step_bytes_per_param(n, 4) == 4 * n + 26
+        # run as three passes: + the fp32 gradient written and read back (8)
+        # and the master read a second time for the parameter write (4)
+        assert ledger.unfused_step_bytes_per_param(n) == 2 * n + 38
+        assert ledger.unfused_step_bytes_per_param(n, 4) == ledger.shard_step_bytes_per_param(n, 4) + 12
