@@ -661,8 +661,16 @@ void shard_step_m16_kernel(StepArgs a)
 //
 // KC (extended step only): -1 flat rank order, 0 two-level with the group
 // size at run time, > 0 two-level with that group size.
-template <zero_dtype G, int NC, bool EXT, int KC = -1>
-__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+//
+// W: resident waves per SIMD.  A launch of at most ZERO_SMALL_LAUNCH_CHUNKS
+// chunks (a small shard, or one gradient bucket) runs two: with few
+// workgroups per CU the launch's ramp and tail weigh more than the
+// read/write mix.  Measured on MI355X, N = 8 bf16, chunks of 2048, one
+// process: 4M-element shards 0.54-0.57 of HBM peak with one wave against
+// 0.64-0.67 with two, 16M 0.65-0.69 against 0.74-0.77, 32M about even,
+// 128M and more 0.69-0.72 against 0.67.
+template <zero_dtype G, int NC, bool EXT, int KC = -1, int W = 1>
+__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, W)))
 void shard_step_kernel(StepArgs a)
 {
     for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
@@ -675,12 +683,13 @@ void shard_step_kernel(StepArgs a)
 // whichever step the index names when it replays.  An index outside the
 // table leaves everything untouched.  L: the state layout (0: fp32 master,
 // m, v; 1: fp32 master, bf16 m, v; 2: pure bf16 with compensation), each
-// with the occupancy of its launch-argument kernel.
-template <int L, zero_dtype G, int NC>
-constexpr int kSchedWaves = L == 0 ? 1 : (L == 1 ? kM16Waves<G, NC> : kKahanWaves);
+// with the occupancy of its launch-argument kernel (W: the 16-byte step's,
+// chosen per launch as for shard_step_kernel).
+template <int L, zero_dtype G, int NC, int W>
+constexpr int kSchedWaves = L == 0 ? W : (L == 1 ? kM16Waves<G, NC> : kKahanWaves);
 
-template <int L, zero_dtype G, int NC>
-__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, kSchedWaves<L, G, NC>)))
+template <int L, zero_dtype G, int NC, int W>
+__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, kSchedWaves<L, G, NC, W>)))
 void shard_step_sched_kernel(StepArgs a)
 {
     const int64_t t = *(const_i64 *)a.sched_index;
@@ -863,42 +872,44 @@ static unsigned chunk_grid(int64_t n_chunks)
     return (unsigned)(n_chunks < kMaxChunkGrid ? n_chunks : kMaxChunkGrid);
 }
 
-template <zero_dtype G, bool EXT>
+template <zero_dtype G, int W>
 static hipError_t step_dispatch(const StepArgs &a, hipStream_t s)
 {
     dim3 grid(chunk_grid(a.n_chunks)), block(kStepBlock);
     switch (a.red.n_ranks) {
-    case 1: hipLaunchKernelGGL((shard_step_kernel<G, 1, EXT>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((shard_step_kernel<G, 2, EXT>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((shard_step_kernel<G, 4, EXT>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((shard_step_kernel<G, 8, EXT>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((shard_step_kernel<G, 16, EXT>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((shard_step_kernel<G, 32, EXT>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((shard_step_kernel<G, 64, EXT>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((shard_step_kernel<G, 0, EXT>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((shard_step_kernel<G, 1, false, -1, W>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((shard_step_kernel<G, 2, false, -1, W>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((shard_step_kernel<G, 4, false, -1, W>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((shard_step_kernel<G, 8, false, -1, W>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((shard_step_kernel<G, 16, false, -1, W>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((shard_step_kernel<G, 32, false, -1, W>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((shard_step_kernel<G, 64, false, -1, W>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((shard_step_kernel<G, 0, false, -1, W>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_step(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 {
-    return gdt == ZERO_BF16 ? step_dispatch<ZERO_BF16, false>(a, s)
-                            : step_dispatch<ZERO_FP32, false>(a, s);
+    const bool small = a.n_chunks <= ZERO_SMALL_LAUNCH_CHUNKS;
+    if (gdt == ZERO_BF16)
+        return small ? step_dispatch<ZERO_BF16, 2>(a, s) : step_dispatch<ZERO_BF16, 1>(a, s);
+    return small ? step_dispatch<ZERO_FP32, 2>(a, s) : step_dispatch<ZERO_FP32, 1>(a, s);
 }
 
-template <int L, zero_dtype G>
+template <int L, zero_dtype G, int W>
 static hipError_t step_sched_dispatch(const StepArgs &a, hipStream_t s)
 {
     dim3 grid(chunk_grid(a.n_chunks)), block(kStepBlock);
     switch (a.red.n_ranks) {
-    case 1: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 8>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 16>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 32>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 64>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 0>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 1, W>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 2, W>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 4, W>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 8, W>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 16, W>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 32, W>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 64, W>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 0, W>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }
@@ -906,8 +917,16 @@ static hipError_t step_sched_dispatch(const StepArgs &a, hipStream_t s)
 template <int L>
 static hipError_t step_sched_layout(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 {
-    return gdt == ZERO_BF16 ? step_sched_dispatch<L, ZERO_BF16>(a, s)
-                            : step_sched_dispatch<L, ZERO_FP32>(a, s);
+    if constexpr (L == 0) {
+        const bool small = a.n_chunks <= ZERO_SMALL_LAUNCH_CHUNKS;
+        if (gdt == ZERO_BF16)
+            return small ? step_sched_dispatch<0, ZERO_BF16, 2>(a, s)
+                         : step_sched_dispatch<0, ZERO_BF16, 1>(a, s);
+        return small ? step_sched_dispatch<0, ZERO_FP32, 2>(a, s)
+                     : step_sched_dispatch<0, ZERO_FP32, 1>(a, s);
+    }
+    return gdt == ZERO_BF16 ? step_sched_dispatch<L, ZERO_BF16, 0>(a, s)
+                            : step_sched_dispatch<L, ZERO_FP32, 0>(a, s);
 }
 
 hipError_t launch_step_sched(const StepArgs &a, zero_dtype gdt, StateLayout layout, hipStream_t s)

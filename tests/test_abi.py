@@ -458,3 +458,16 @@ def test_scheduled_layouts_share_the_checks(zs):
         assert call(v=m + 1984) == zs.ZERO_ERR_ALIAS              # bf16 m spans 2000 bytes
         assert call(v=m + 2000) == zs.ZERO_ERR_NOT_DEVICE
         assert call(index=m + 1992) == zs.ZERO_ERR_ALIAS
+
+
+def test_header_constants_match_the_binding(zs):
+    """Every integer #define of the header has the same value in the Python
+    binding."""
+    text = open(HEADER).read()
+    found = re.findall(r"^#define (ZERO_[A-Z_]+)\s+([^/\n]+)", text, flags=re.M)
+    assert len(found) >= 4
+    for name, value in found:
+        if name == "ZERO_SHARD_H":
+            continue
+        v = eval(value.replace("(int64_t)", "").strip(), {})   # integer expression only
+        assert getattr(zs, name) == v, name

@@ -8,6 +8,12 @@ one, and runs every fused entry point on it: the 16-byte step, the 12-byte
 step, the pure-bf16 Kahan step, and the extended step with every group size
 the dispatcher distinguishes for that N (flat, compiled 4, compiled 8, a
 group size folded at run time), each with one accumulated micro-batch.
+
+The 16-byte step also compiles two occupancies: launches of at most
+ZERO_SMALL_LAUNCH_CHUNKS chunks run two waves per SIMD, longer ones one.
+The small cases take the first; a second case per (dtype, N) builds a
+table just over that many chunks to take the other, for the launch-argument
+and the scheduled forms.
 """
 import numpy as np
 import pytest
@@ -125,3 +131,41 @@ def test_every_compiled_variant(zs, gdt, n_ranks):
         for got, want, what in ((host(master), th, "master"), (host(m), mm, "m"),
                                 (host(v), vv, "v"), (host(full)[lo:hi], p, "param")):
             assert_bitwise(got, want, f"{tag} extended group {k} {what}")
+
+
+@pytest.mark.parametrize("gdt", ["bf16", "f32"])
+@pytest.mark.parametrize("n_ranks", RANKS)
+def test_one_wave_variant_over_a_long_table(zs, gdt, n_ranks):
+    n = zs.ZERO_SMALL_LAUNCH_CHUNKS * 64 + 777      # chunks of 64: just over the limit
+    w = W.Workload("variants-long", 97, [n * n_ranks], n_ranks, gdt, 1e-3)
+    lo, hi = w.shard_range(0)
+    assert hi - lo == n
+    idx = np.arange(lo, hi, dtype=np.int64)
+    slot = torch.full((n,), -1, dtype=torch.int16, device="cuda")
+    table, _ = zs.zero_build_chunks([n * n_ranks], n_ranks, 0, slot_dst=slot, max_chunk=64)
+    assert len(table) > zs.ZERO_SMALL_LAUNCH_CHUNKS
+    d_table, nc = zs.chunks_to_device(table), len(table)
+    t = 3
+    parts_h = host_partials(w, t, idx)
+    parts = [dev(p) for p in parts_h]
+    th0 = host_master(w, idx)
+    rng = np.random.default_rng(n_ranks)
+    m0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v0 = (rng.random(n) * 1e-8).astype(np.float32)
+    th, mm, vv, p = oracle.shard_step(parts_h, th0, m0, v0, oracle.hparams(t, **HP))
+    tag = f"N={n_ranks} {gdt}, {nc} chunks"
+    say(f"case: variants {tag}: 16-byte step, one wave per SIMD")
+    master, m, v = dev(th0), dev(m0), dev(v0)
+    zs.zero_shard_step(parts, master, m, v, n, d_table, nc, zs.hparams(t, **HP))
+    for got, want, what in ((host(master), th, "master"), (host(m), mm, "m"), (host(v), vv, "v"),
+                            (host(slot), p, "param")):
+        assert_bitwise(got, want, f"{tag} {what}")
+    say(f"case: variants {tag}: scheduled 16-byte step, one wave per SIMD")
+    consts = torch.from_numpy(zs.zero_make_step_consts([zs.hparams(t, **HP)]).view(np.uint8)).cuda()
+    index = torch.zeros(1, dtype=torch.int64, device="cuda")
+    slot.fill_(-1)
+    master, m, v = dev(th0), dev(m0), dev(v0)
+    zs.zero_shard_step_scheduled(parts, master, m, v, n, d_table, nc, consts, 1, index)
+    for got, want, what in ((host(master), th, "master"), (host(m), mm, "m"), (host(v), vv, "v"),
+                            (host(slot), p, "param")):
+        assert_bitwise(got, want, f"{tag} scheduled {what}")
