@@ -188,8 +188,9 @@ int zero_build_chunks(const int64_t *numels, int n_tensors, int n_ranks, int ran
  *            are left untouched.
  * hp:        host pointer to the hyper-parameters of this step.
  * Errors: INVALID (null, n_ranks out of range, shard_len < 0 or above
- * ZERO_MAX_LEN, n_chunks < 0 or above INT32_MAX, bad hp), MISALIGNED, UNSUPPORTED (gdt), NOT_DEVICE, ALIAS (a partial overlaps master,
- * m or v, or those overlap each other), HIP.
+ * ZERO_MAX_LEN, n_chunks < 0 or above INT32_MAX, bad hp), MISALIGNED,
+ * UNSUPPORTED (gdt), ALIAS (a partial overlaps master, m or v, or those
+ * overlap each other), NOT_DEVICE, HIP.
  */
 int zero_shard_step(const void *const *partials, int n_ranks, int gdt,
                     float *master, float *m, float *v, int64_t shard_len,

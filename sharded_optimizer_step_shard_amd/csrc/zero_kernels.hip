@@ -654,10 +654,10 @@ void shard_step_m16_kernel(StepArgs a)
 //
 // On large launches the 16-byte step keeps at most one wave per SIMD
 // (waves_per_eu): with fewer concurrent streams the HBM sustains more of its
-// peak on this mixed read/write stream.  Measured on MI355X across chunk sizes and block
-// shapes, 4 resident waves per CU beat 8-16 (7B shard: 0.71 against 0.63-0.64
-// with two to four waves per SIMD).  Each wave still keeps its group's 14
-// (N = 8) to 22 (N = 16) 16-byte loads in flight at once.
+// peak on this mixed read/write stream.  Measured on MI355X across chunk
+// sizes and block shapes, 4 resident waves per CU beat 8-16 (7B shard: 0.71
+// against 0.63-0.64 with two to four waves per SIMD).  Each wave still keeps
+// its group's 14 (N = 8) to 22 (N = 16) 16-byte loads in flight at once.
 //
 // KC (extended step only): -1 flat rank order, 0 two-level with the group
 // size at run time, > 0 two-level with that group size.
