@@ -37,10 +37,12 @@ from synth import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 # What decides the step kernels' HBM traffic: the kernels, their argument
-# layout, and how the chunk table is cut.  Recorded counters stay valid while
-# the code (not the comments) of these files is unchanged.
+# layout, how the chunk table is cut, and the public header (the chunk
+# record, the launch-size limits).  Recorded counters stay valid while the
+# code (not the comments) of these files is unchanged.
 KERNEL_SOURCES = [os.path.join(ROOT, "sharded_optimizer_step_shard_amd", "csrc", f)
-                  for f in ("zero_kernels.hip", "zero_internal.h", "zero_chunks.cpp")]
+                  for f in ("zero_kernels.hip", "zero_internal.h", "zero_chunks.cpp")] + \
+                 [os.path.join(ROOT, "include", "zero_shard.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # Optimizer-state layouts the fused step runs on: the kernel, the state bytes
