@@ -513,16 +513,24 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
 // with three; with 16 partials (70B) the 12-byte step is best with one wave
 // (0.725 against 0.69), the pure-bf16 step with two (0.63 -> 0.71; its
 // registers allow no third).
-template <zero_dtype G, int NC>
-constexpr int kM16Waves = (NC > 0 && NC * Grad<G>::BYTES <= 16) ? 2 : 1;
+//
+// SMALL: a launch of at most ZERO_SMALL_LAUNCH_CHUNKS chunks, where the
+// launch's ramp and tail weigh more; there the 12-byte step with few
+// partials runs three waves with batches of 8.  Measured (N = 8 bf16,
+// chunks of 2048, one process, two waves / three): 4M-element shards
+// 0.51-0.52 / 0.56-0.59, 16M 0.55-0.63 / 0.69-0.71, 32M 0.61-0.64 /
+// 0.69-0.79, 128M and 256M 0.64-0.69 / 0.67-0.68.  The pure-bf16 step gained
+// nothing from two or four waves on the GPT-2 shard.
+template <zero_dtype G, int NC, bool SMALL>
+constexpr int kM16Waves = (NC > 0 && NC * Grad<G>::BYTES <= 16) ? (SMALL ? 3 : 2) : 1;
 constexpr int kKahanWaves = 3;
-template <zero_dtype G, int NC>
-constexpr int kM16Batch = kM16Waves<G, NC> == 2 ? 2 : kStepBatch;
+template <zero_dtype G, int NC, bool SMALL>
+constexpr int kM16Batch = kM16Waves<G, NC, SMALL> == 2 ? 2 : kStepBatch;
 
 // The step on the 12-byte state: fp32 master, bf16 m and v (in a.m, a.v
 // as 16-bit patterns).  Same reduce and AdamW; the moments are read from
 // bf16 and rounded back to bf16 once, from double.
-template <zero_dtype G, int NC>
+template <zero_dtype G, int NC, bool SMALL>
 __device__ __forceinline__ void step_chunk_m16(const StepArgs &a, const zero_chunk &c,
                                                const StepScalars &k)
 {
@@ -544,7 +552,7 @@ __device__ __forceinline__ void step_chunk_m16(const StepArgs &a, const zero_chu
             th.load(a.master + i0);
             m.load(m16 + i0);
             v.load(v16 + i0);
-            group_sum<G, NC, kM16Batch<G, NC>>(s, a.parts, n, i0);
+            group_sum<G, NC, kM16Batch<G, NC, SMALL>>(s, a.parts, n, i0);
             uint32_t h[VEC];
 #pragma unroll
             for (int j = 0; j < VEC; ++j) {
@@ -640,12 +648,12 @@ void shard_step_kahan_kernel(StepArgs a)
         step_chunk_kahan<G, NC>(a, chunk_at(a.chunks, ci), a.k);
 }
 
-template <zero_dtype G, int NC>
-__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, kM16Waves<G, NC>)))
+template <zero_dtype G, int NC, bool SMALL>
+__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, kM16Waves<G, NC, SMALL>)))
 void shard_step_m16_kernel(StepArgs a)
 {
     for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
-        step_chunk_m16<G, NC>(a, chunk_at(a.chunks, ci), a.k);
+        step_chunk_m16<G, NC, SMALL>(a, chunk_at(a.chunks, ci), a.k);
 }
 
 // In every chunk-table kernel a workgroup (one wave) takes chunks
@@ -683,13 +691,14 @@ void shard_step_kernel(StepArgs a)
 // whichever step the index names when it replays.  An index outside the
 // table leaves everything untouched.  L: the state layout (0: fp32 master,
 // m, v; 1: fp32 master, bf16 m, v; 2: pure bf16 with compensation), each
-// with the occupancy of its launch-argument kernel (W: the 16-byte step's,
-// chosen per launch as for shard_step_kernel).
-template <int L, zero_dtype G, int NC, int W>
-constexpr int kSchedWaves = L == 0 ? W : (L == 1 ? kM16Waves<G, NC> : kKahanWaves);
+// with the occupancy of its launch-argument kernel (SMALL: chosen per
+// launch as for those kernels).
+template <int L, zero_dtype G, int NC, bool SMALL>
+constexpr int kSchedWaves = L == 0 ? (SMALL ? 2 : 1)
+                                   : (L == 1 ? kM16Waves<G, NC, SMALL> : kKahanWaves);
 
-template <int L, zero_dtype G, int NC, int W>
-__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, kSchedWaves<L, G, NC, W>)))
+template <int L, zero_dtype G, int NC, bool SMALL>
+__global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, kSchedWaves<L, G, NC, SMALL>)))
 void shard_step_sched_kernel(StepArgs a)
 {
     const int64_t t = *(const_i64 *)a.sched_index;
@@ -703,7 +712,7 @@ void shard_step_sched_kernel(StepArgs a)
         if constexpr (L == 0)
             step_chunk<G, NC, false, -1>(a, chunk_at(a.chunks, ci), k);
         else if constexpr (L == 1)
-            step_chunk_m16<G, NC>(a, chunk_at(a.chunks, ci), k);
+            step_chunk_m16<G, NC, SMALL>(a, chunk_at(a.chunks, ci), k);
         else
             step_chunk_kahan<G, NC>(a, chunk_at(a.chunks, ci), k);
     }
@@ -897,19 +906,19 @@ hipError_t launch_step(const StepArgs &a, zero_dtype gdt, hipStream_t s)
     return small ? step_dispatch<ZERO_FP32, 2>(a, s) : step_dispatch<ZERO_FP32, 1>(a, s);
 }
 
-template <int L, zero_dtype G, int W>
+template <int L, zero_dtype G, bool SMALL>
 static hipError_t step_sched_dispatch(const StepArgs &a, hipStream_t s)
 {
     dim3 grid(chunk_grid(a.n_chunks)), block(kStepBlock);
     switch (a.red.n_ranks) {
-    case 1: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 1, W>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 2, W>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 4, W>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 8, W>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 16, W>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 32, W>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 64, W>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 0, W>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 1, SMALL>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 2, SMALL>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 4, SMALL>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 8, SMALL>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 16, SMALL>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 32, SMALL>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 64, SMALL>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((shard_step_sched_kernel<L, G, 0, SMALL>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }
@@ -917,16 +926,12 @@ static hipError_t step_sched_dispatch(const StepArgs &a, hipStream_t s)
 template <int L>
 static hipError_t step_sched_layout(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 {
-    if constexpr (L == 0) {
-        const bool small = a.n_chunks <= ZERO_SMALL_LAUNCH_CHUNKS;
-        if (gdt == ZERO_BF16)
-            return small ? step_sched_dispatch<0, ZERO_BF16, 2>(a, s)
-                         : step_sched_dispatch<0, ZERO_BF16, 1>(a, s);
-        return small ? step_sched_dispatch<0, ZERO_FP32, 2>(a, s)
-                     : step_sched_dispatch<0, ZERO_FP32, 1>(a, s);
-    }
-    return gdt == ZERO_BF16 ? step_sched_dispatch<L, ZERO_BF16, 0>(a, s)
-                            : step_sched_dispatch<L, ZERO_FP32, 0>(a, s);
+    const bool small = a.n_chunks <= ZERO_SMALL_LAUNCH_CHUNKS;
+    if (gdt == ZERO_BF16)
+        return small ? step_sched_dispatch<L, ZERO_BF16, true>(a, s)
+                     : step_sched_dispatch<L, ZERO_BF16, false>(a, s);
+    return small ? step_sched_dispatch<L, ZERO_FP32, true>(a, s)
+                 : step_sched_dispatch<L, ZERO_FP32, false>(a, s);
 }
 
 hipError_t launch_step_sched(const StepArgs &a, zero_dtype gdt, StateLayout layout, hipStream_t s)
@@ -985,19 +990,19 @@ static hipError_t step_ex_dispatch(const StepArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <zero_dtype G>
+template <zero_dtype G, bool SMALL>
 static hipError_t step_m16_dispatch(const StepArgs &a, hipStream_t s)
 {
     dim3 grid(chunk_grid(a.n_chunks)), block(kStepBlock);
     switch (a.red.n_ranks) {
-    case 1: hipLaunchKernelGGL((shard_step_m16_kernel<G, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((shard_step_m16_kernel<G, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((shard_step_m16_kernel<G, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((shard_step_m16_kernel<G, 8>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((shard_step_m16_kernel<G, 16>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((shard_step_m16_kernel<G, 32>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((shard_step_m16_kernel<G, 64>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((shard_step_m16_kernel<G, 0>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((shard_step_m16_kernel<G, 1, SMALL>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((shard_step_m16_kernel<G, 2, SMALL>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((shard_step_m16_kernel<G, 4, SMALL>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((shard_step_m16_kernel<G, 8, SMALL>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((shard_step_m16_kernel<G, 16, SMALL>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((shard_step_m16_kernel<G, 32, SMALL>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((shard_step_m16_kernel<G, 64, SMALL>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((shard_step_m16_kernel<G, 0, SMALL>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }
@@ -1026,7 +1031,10 @@ hipError_t launch_step_kahan(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 
 hipError_t launch_step_m16(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 {
-    return gdt == ZERO_BF16 ? step_m16_dispatch<ZERO_BF16>(a, s) : step_m16_dispatch<ZERO_FP32>(a, s);
+    const bool small = a.n_chunks <= ZERO_SMALL_LAUNCH_CHUNKS;
+    if (gdt == ZERO_BF16)
+        return small ? step_m16_dispatch<ZERO_BF16, true>(a, s) : step_m16_dispatch<ZERO_BF16, false>(a, s);
+    return small ? step_m16_dispatch<ZERO_FP32, true>(a, s) : step_m16_dispatch<ZERO_FP32, false>(a, s);
 }
 
 hipError_t launch_step_ex(const StepArgs &a, zero_dtype gdt, hipStream_t s)

@@ -9,11 +9,11 @@ step, the pure-bf16 Kahan step, and the extended step with every group size
 the dispatcher distinguishes for that N (flat, compiled 4, compiled 8, a
 group size folded at run time), each with one accumulated micro-batch.
 
-The 16-byte step also compiles two occupancies: launches of at most
-ZERO_SMALL_LAUNCH_CHUNKS chunks run two waves per SIMD, longer ones one.
-The small cases take the first; a second case per (dtype, N) builds a
-table just over that many chunks to take the other, for the launch-argument
-and the scheduled forms.
+The 16-byte and 12-byte steps also compile two occupancies each: launches
+of at most ZERO_SMALL_LAUNCH_CHUNKS chunks run more waves per SIMD than
+longer ones.  The small cases take the first; a second case per (dtype, N)
+builds a table just over that many chunks to take the other, for the
+launch-argument and the scheduled forms of both steps.
 """
 import numpy as np
 import pytest
@@ -135,7 +135,7 @@ def test_every_compiled_variant(zs, gdt, n_ranks):
 
 @pytest.mark.parametrize("gdt", ["bf16", "f32"])
 @pytest.mark.parametrize("n_ranks", RANKS)
-def test_one_wave_variant_over_a_long_table(zs, gdt, n_ranks):
+def test_large_launch_variants_over_a_long_table(zs, gdt, n_ranks):
     n = zs.ZERO_SMALL_LAUNCH_CHUNKS * 64 + 777      # chunks of 64: just over the limit
     w = W.Workload("variants-long", 97, [n * n_ranks], n_ranks, gdt, 1e-3)
     lo, hi = w.shard_range(0)
@@ -154,13 +154,13 @@ def test_one_wave_variant_over_a_long_table(zs, gdt, n_ranks):
     v0 = (rng.random(n) * 1e-8).astype(np.float32)
     th, mm, vv, p = oracle.shard_step(parts_h, th0, m0, v0, oracle.hparams(t, **HP))
     tag = f"N={n_ranks} {gdt}, {nc} chunks"
-    say(f"case: variants {tag}: 16-byte step, one wave per SIMD")
+    say(f"case: variants {tag}: 16-byte step, large-launch occupancy")
     master, m, v = dev(th0), dev(m0), dev(v0)
     zs.zero_shard_step(parts, master, m, v, n, d_table, nc, zs.hparams(t, **HP))
     for got, want, what in ((host(master), th, "master"), (host(m), mm, "m"), (host(v), vv, "v"),
                             (host(slot), p, "param")):
         assert_bitwise(got, want, f"{tag} {what}")
-    say(f"case: variants {tag}: scheduled 16-byte step, one wave per SIMD")
+    say(f"case: variants {tag}: scheduled 16-byte step, large-launch occupancy")
     consts = torch.from_numpy(zs.zero_make_step_consts([zs.hparams(t, **HP)]).view(np.uint8)).cuda()
     index = torch.zeros(1, dtype=torch.int64, device="cuda")
     slot.fill_(-1)
@@ -169,3 +169,18 @@ def test_one_wave_variant_over_a_long_table(zs, gdt, n_ranks):
     for got, want, what in ((host(master), th, "master"), (host(m), mm, "m"), (host(v), vv, "v"),
                             (host(slot), p, "param")):
         assert_bitwise(got, want, f"{tag} scheduled {what}")
+    say(f"case: variants {tag}: 12-byte step and its scheduled form, large-launch occupancy")
+    m16, v16 = oracle.bf16_from_double(m0), oracle.bf16_from_double(v0)
+    th, mm, vv, p = oracle.shard_step_bf16m(parts_h, th0, m16, v16, oracle.hparams(t, **HP))
+    for scheduled in (False, True):
+        slot.fill_(-1)
+        master, m, v = dev(th0), dev(m16), dev(v16)
+        if scheduled:
+            index.zero_()
+            zs.zero_shard_step_bf16_moments_scheduled(parts, master, m, v, n, d_table, nc, consts, 1,
+                                                      index)
+        else:
+            zs.zero_shard_step_bf16_moments(parts, master, m, v, n, d_table, nc, zs.hparams(t, **HP))
+        for got, want, what in ((host(master), th, "master"), (host(m), mm, "m"),
+                                (host(v), vv, "v"), (host(slot), p, "param")):
+            assert_bitwise(got, want, f"{tag} 12-byte{' scheduled' if scheduled else ''} {what}")
