@@ -29,7 +29,7 @@ ZERO_ERR_ALIAS, ZERO_ERR_HIP, ZERO_ERR_CAPACITY, ZERO_ERR_NOT_DEVICE = 4, 5, 6, 
 ZERO_MAX_RANKS = 64
 ZERO_MAX_LEN = 1 << 48          # largest element or byte count an entry point accepts
 ZERO_DEFAULT_MAX_CHUNK = 2048
-ZERO_SMALL_LAUNCH_CHUNKS = 16384  # 16-byte step launches up to this many chunks run two waves per SIMD
+ZERO_SMALL_LAUNCH_CHUNKS = 16384  # step launches up to this many chunks run at a higher occupancy
 
 # Mirrors `zero_chunk` (32 bytes).
 CHUNK_DTYPE = np.dtype([("shard_off", "<i8"), ("dst", "<u8"), ("len", "<i4"),
