@@ -138,10 +138,10 @@ enum {
 #define ZERO_MAX_RANKS 64
 #define ZERO_MAX_LEN (((int64_t)1) << 48)   /* largest element or byte count */
 #define ZERO_DEFAULT_MAX_CHUNK 2048   /* chunk length the step kernel is tuned for */
-/* Launches of the 16-byte and 12-byte steps (with their bucket and
- * scheduled forms) over at most this many chunks run at a higher occupancy,
- * which suits small shards and single gradient buckets.  Results are the
- * same bits either way. */
+/* Launches of the 16-byte, 12-byte and extended steps (with their bucket
+ * and scheduled forms) over at most this many chunks run at a higher
+ * occupancy, which suits small shards and single gradient buckets.  Results
+ * are the same bits either way. */
 #define ZERO_SMALL_LAUNCH_CHUNKS 16384
 
 /*

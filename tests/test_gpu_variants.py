@@ -9,11 +9,12 @@ step, the pure-bf16 Kahan step, and the extended step with every group size
 the dispatcher distinguishes for that N (flat, compiled 4, compiled 8, a
 group size folded at run time), each with one accumulated micro-batch.
 
-The 16-byte and 12-byte steps also compile two occupancies each: launches
-of at most ZERO_SMALL_LAUNCH_CHUNKS chunks run more waves per SIMD than
-longer ones.  The small cases take the first; a second case per (dtype, N)
-builds a table just over that many chunks to take the other, for the
-launch-argument and the scheduled forms of both steps.
+The 16-byte, 12-byte and extended steps also compile two occupancies
+each: launches of at most ZERO_SMALL_LAUNCH_CHUNKS chunks run more waves
+per SIMD than longer ones.  The small cases take the first; a second case
+per (dtype, N) builds a table just over that many chunks to take the other,
+for the launch-argument and scheduled forms and every fold of the
+extended step.
 """
 import numpy as np
 import pytest
@@ -184,3 +185,18 @@ def test_large_launch_variants_over_a_long_table(zs, gdt, n_ranks):
         for got, want, what in ((host(master), th, "master"), (host(m), mm, "m"),
                                 (host(v), vv, "v"), (host(slot), p, "param")):
             assert_bitwise(got, want, f"{tag} 12-byte{' scheduled' if scheduled else ''} {what}")
+    for k in groups_for(n_ranks):
+        say(f"case: variants {tag}: extended step, group {k or 'flat'}, large-launch occupancy")
+        acc = torch.empty(n, dtype=torch.float32, device="cuda")
+        prev_h = [x[::-1].copy() for x in parts_h]            # an earlier micro-batch
+        zs.zero_accumulate_shard([dev(x) for x in prev_h], n, acc, reset=True, group=k)
+        acc_h = oracle.accumulate(prev_h, None, group=k or None)
+        slot.fill_(-1)
+        master, m, v = dev(th0), dev(m0), dev(v0)
+        zs.zero_shard_step_ex(parts, master, m, v, n, d_table, nc, zs.hparams(t, **HP), group=k,
+                              micro_batches=2, acc=acc)
+        th, mm, vv, p = oracle.shard_step_ex(parts_h, th0, m0, v0, oracle.hparams(t, **HP),
+                                             group=k or None, acc=acc_h, micro_batches=2)
+        for got, want, what in ((host(master), th, "master"), (host(m), mm, "m"),
+                                (host(v), vv, "v"), (host(slot), p, "param")):
+            assert_bitwise(got, want, f"{tag} extended group {k} {what}")
