@@ -471,3 +471,28 @@ def test_header_constants_match_the_binding(zs):
             continue
         v = eval(value.replace("(int64_t)", "").strip(), {})   # integer expression only
         assert getattr(zs, name) == v, name
+
+
+@pytest.mark.parametrize("name", ["zero_shard_step", "zero_shard_step_bf16_moments",
+                                  "zero_shard_step_kahan", "zero_shard_step_scheduled",
+                                  "zero_shard_step_bf16_moments_scheduled",
+                                  "zero_shard_step_kahan_scheduled"])
+def test_fused_steps_check_in_the_documented_order(zs, name):
+    """Every fused step, with several faults at once, returns the first in
+    the header's order: INVALID, MISALIGNED, UNSUPPORTED, ALIAS, NOT_DEVICE."""
+    scheduled = name.endswith("_scheduled")
+    hp = zs.hparams(1)
+    consts, index = BASE + (3 << 40), BASE + (3 << 40) + (1 << 20)
+
+    def call(p, gdt=0, first=BASE + (1 << 40), n=1000):
+        tail = ((consts, 4, index, None) if scheduled else (ctypes.byref(hp), None))
+        return zs.raw_call(name, p, 4, gdt, first, BASE + (1 << 40) + (1 << 32),
+                           BASE + (1 << 40) + (2 << 32), n, BASE + (1 << 41), 1, *tail)
+    p, mis = parts(4), parts(4)
+    mis[1] = BASE + (1 << 30) + 8
+    assert call(mis, gdt=9, first=None) == zs.ZERO_ERR_INVALID
+    assert call(mis, gdt=9, first=BASE) == zs.ZERO_ERR_MISALIGNED
+    assert call(p, gdt=9, first=BASE) == zs.ZERO_ERR_UNSUPPORTED
+    assert call(p, first=BASE) == zs.ZERO_ERR_ALIAS
+    assert call(p) == zs.ZERO_ERR_NOT_DEVICE
+    assert call(p, n=-5, gdt=9, first=BASE + 4) == zs.ZERO_ERR_INVALID
