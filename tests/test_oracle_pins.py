@@ -400,3 +400,22 @@ def test_shard_step_byte_model():
         # and the master read a second time for the parameter write (4)
         assert ledger.unfused_step_bytes_per_param(n) == 2 * n + 38
         assert ledger.unfused_step_bytes_per_param(n, 4) == ledger.shard_step_bytes_per_param(n, 4) + 12
+
+
+def test_power_of_two_mean_is_a_scaling():
+    """The mean's divisor, for a power-of-two count (N, or N times the
+    micro-batches), is an exact scaling in double: s / 2^k equals s * 2^-k
+    bit for bit at every magnitude a sum of bf16 or fp32 values can take, so
+    a kernel may multiply where the definition divides (reading of the
+    mean, §3 #5).  For other counts the two differ, so the division stays."""
+    rng = np.random.default_rng(11)
+    s = np.ldexp(rng.uniform(1.0, 2.0, 200_000) * rng.choice([-1.0, 1.0], 200_000),
+                 rng.integers(-160, 140, 200_000))
+    for k in range(0, 41):
+        n = float(2 ** k)
+        assert np.array_equal((s / n).view(np.uint64), (s * (1.0 / n)).view(np.uint64)), k
+        with np.errstate(over="ignore"):              # sums past fp32's range round to inf
+            assert np.array_equal((s / n).astype(np.float32).view(np.uint32),
+                                  (s * (1.0 / n)).astype(np.float32).view(np.uint32)), k
+    differs = [n for n in (3, 5, 6, 7, 12, 24, 48) if not np.array_equal(s / n, s * (1.0 / n))]
+    assert differs == [3, 5, 6, 7, 12, 24, 48]
