@@ -22,12 +22,35 @@ __device__ __forceinline__ T ld(const T *p) { return *p; }
 template <typename T>
 __device__ __forceinline__ void st_nt(T *p, T x) { __builtin_nontemporal_store(x, p); }
 
-__global__ __launch_bounds__(kBlock) void probe_copy_kernel(const u32x4 *src, u32x4 *dst, int64_t n16,
-                                                            const uint8_t *src_b, uint8_t *dst_b,
-                                                            int64_t bytes)
+// Copy stream (also the known-size traffic that calibrates the HBM
+// counters): one wave per SIMD; wave b copies 8 KiB pieces b, b + gridDim.x,
+// ... with 8 non-temporal 16-byte loads in flight per lane, then their 8
+// non-temporal stores.  Measured on MI355X: 5.4 TB/s (read plus written)
+// against 5.0 for one plain load and store per lane in 256-lane workgroups.
+// The bytes past the last full word are copied element by element.
+constexpr int kCopyLanes = 64;
+constexpr int kCopyUnroll = 8;
+constexpr int64_t kCopyPiece = kCopyLanes * kCopyUnroll;   // 16-byte words per piece
+
+__global__ __launch_bounds__(kCopyLanes) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void probe_copy_kernel(const u32x4 *src, u32x4 *dst, int64_t n16, const uint8_t *src_b,
+                       uint8_t *dst_b, int64_t bytes)
 {
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n16; i += (int64_t)gridDim.x * kBlock)
-        st_nt(dst + i, ld(src + i));
+    for (int64_t p = blockIdx.x; p * kCopyPiece < n16; p += gridDim.x) {
+        u32x4 r[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const int64_t i = p * kCopyPiece + u * kCopyLanes + threadIdx.x;
+            r[u] = i < n16 ? __builtin_nontemporal_load(src + i) : (u32x4){0u, 0u, 0u, 0u};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const int64_t i = p * kCopyPiece + u * kCopyLanes + threadIdx.x;
+            if (i < n16)
+                st_nt(dst + i, r[u]);
+        }
+    }
     if (blockIdx.x == 0) {
         const int64_t b = n16 * 16 + threadIdx.x;
         if (b < bytes)
@@ -35,22 +58,33 @@ __global__ __launch_bounds__(kBlock) void probe_copy_kernel(const u32x4 *src, u3
     }
 }
 
-// Read-only stream: workgroup b reads 4 KiB pieces b, b + gridDim.x, ...
-// (one 16-byte load per lane), folding them by XOR into a value that is
-// stored only if it equals `magic`, so the loads cannot be dropped and in
-// practice nothing is written.  Many short contiguous pieces per workgroup
-// sustained the highest read rate among the shapes measured on MI355X.
-constexpr int kReadPiece = kBlock;     // 16-byte words per piece (4 KiB)
+// Read-only stream: one wave per SIMD; wave b reads 8 KiB pieces b,
+// b + gridDim.x, ... with 8 non-temporal 16-byte loads in flight per lane,
+// folding them by XOR into a value that is stored only if it equals
+// `magic`, so the loads cannot be dropped and in practice nothing is
+// written.  Of the shapes measured on MI355X (one or 4-8 loads per lane,
+// plain or non-temporal, 64- or 256-lane workgroups, 1K-1M workgroups)
+// this one sustained the highest rate: 7.3 TB/s against 6.6 for one plain
+// load per lane in 256-lane workgroups.
+constexpr int kReadLanes = 64;
+constexpr int kReadUnroll = 8;
+constexpr int64_t kReadPiece = kReadLanes * kReadUnroll;   // 16-byte words per piece
 
-__global__ __launch_bounds__(kBlock) void probe_read_kernel(const u32x4 *src, int64_t n16,
-                                                            const uint8_t *src_b, int64_t bytes,
-                                                            uint32_t *sink, uint32_t magic)
+__global__ __launch_bounds__(kReadLanes) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void probe_read_kernel(const u32x4 *src, int64_t n16, const uint8_t *src_b, int64_t bytes,
+                       uint32_t *sink, uint32_t magic)
 {
     u32x4 acc = {0u, 0u, 0u, 0u};
     for (int64_t p = blockIdx.x; p * kReadPiece < n16; p += gridDim.x) {
-        const int64_t i = p * kReadPiece + threadIdx.x;
-        if (i < n16)
-            acc ^= ld(src + i);
+        u32x4 r[kReadUnroll];
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u) {
+            const int64_t i = p * kReadPiece + u * kReadLanes + threadIdx.x;
+            r[u] = i < n16 ? __builtin_nontemporal_load(src + i) : (u32x4){0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u)
+            acc ^= r[u];
     }
     uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
     if (blockIdx.x == 0) {
@@ -62,6 +96,8 @@ __global__ __launch_bounds__(kBlock) void probe_read_kernel(const u32x4 *src, in
         sink[0] = x;
 }
 
+constexpr int64_t kWritePiece = kBlock;     // 16-byte words per piece (4 KiB)
+
 // Write-only stream: workgroup b writes 4 KiB pieces b, b + gridDim.x, ...
 // with one non-temporal 16-byte store per lane (the store the step kernels
 // use for their state), the bytes past the last full word element by
@@ -71,8 +107,8 @@ __global__ __launch_bounds__(kBlock) void probe_write_kernel(u32x4 *dst, int64_t
                                                              uint32_t value)
 {
     const u32x4 w = {value, value, value, value};
-    for (int64_t p = blockIdx.x; p * kReadPiece < n16; p += gridDim.x) {
-        const int64_t i = p * kReadPiece + threadIdx.x;
+    for (int64_t p = blockIdx.x; p * kWritePiece < n16; p += gridDim.x) {
+        const int64_t i = p * kWritePiece + threadIdx.x;
         if (i < n16)
             st_nt(dst + i, w);
     }
@@ -83,21 +119,19 @@ __global__ __launch_bounds__(kBlock) void probe_write_kernel(u32x4 *dst, int64_t
     }
 }
 
-int grid_for(int64_t items)
-{
-    int64_t blocks = (items + kBlock - 1) / kBlock;
-    if (blocks > 256 * 64)
-        blocks = 256 * 64;
-    return blocks < 1 ? 1 : (int)blocks;
-}
-
 }  // namespace
 
 hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s)
 {
     const int64_t n16 = bytes / 16;
-    hipLaunchKernelGGL(probe_copy_kernel, dim3(grid_for(n16 + 1)), dim3(kBlock), 0, s,
-                       (const u32x4 *)src, (u32x4 *)dst, n16, (const uint8_t *)src, (uint8_t *)dst, bytes);
+    int64_t pieces = (n16 + kCopyPiece - 1) / kCopyPiece;
+    if (pieces > 65536)
+        pieces = 65536;
+    if (pieces < 1)
+        pieces = 1;
+    hipLaunchKernelGGL(probe_copy_kernel, dim3((int)pieces), dim3(kCopyLanes), 0, s,
+                       (const u32x4 *)src, (u32x4 *)dst, n16, (const uint8_t *)src, (uint8_t *)dst,
+                       bytes);
     return hipGetLastError();
 }
 
@@ -106,19 +140,19 @@ hipError_t launch_probe_read(const void *src, int64_t bytes, uint32_t *sink, uin
 {
     const int64_t n16 = bytes / 16;
     int64_t pieces = (n16 + kReadPiece - 1) / kReadPiece;
-    if (pieces > (1 << 20))
-        pieces = 1 << 20;
+    if (pieces > 65536)
+        pieces = 65536;
     if (pieces < 1)
         pieces = 1;
-    hipLaunchKernelGGL(probe_read_kernel, dim3((int)pieces), dim3(kBlock), 0, s, (const u32x4 *)src,
-                       n16, (const uint8_t *)src, bytes, sink, magic);
+    hipLaunchKernelGGL(probe_read_kernel, dim3((int)pieces), dim3(kReadLanes), 0, s,
+                       (const u32x4 *)src, n16, (const uint8_t *)src, bytes, sink, magic);
     return hipGetLastError();
 }
 
 hipError_t launch_probe_write(void *dst, int64_t bytes, uint32_t value, hipStream_t s)
 {
     const int64_t n16 = bytes / 16;
-    int64_t pieces = (n16 + kReadPiece - 1) / kReadPiece;
+    int64_t pieces = (n16 + kWritePiece - 1) / kWritePiece;
     if (pieces > (1 << 20))
         pieces = 1 << 20;
     if (pieces < 1)
