@@ -412,9 +412,9 @@ int zero_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t strea
 /*
  * Measurement aid, not part of the step: reads `bytes` bytes at src (device,
  * 16-byte aligned) with a streaming kernel and writes nothing, except that
- * if the XOR of everything one workgroup read equals `magic` it stores that
- * value to *sink (device, 4-byte aligned, caller-owned).  Gives the
- * attainable read-only HBM rate beside the copy rate.
+ * if the XOR of the words one lane read equals `magic` it stores that value
+ * to *sink (device, 4-byte aligned, caller-owned).  Gives the attainable
+ * read-only HBM rate beside the copy rate.
  * Errors: INVALID (null with bytes > 0, bytes < 0), MISALIGNED, NOT_DEVICE.
  */
 int zero_probe_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t magic,
