@@ -891,6 +891,10 @@ def main() -> int:
                      "kernel": kernel_key, "kernel_ms": kernel_ms,
                      "algorithmic_bytes_per_launch": bytes_launch},
     }
+    props = torch.cuda.get_device_properties(0)
+    out["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                     "compute_units": props.multi_processor_count,
+                     "memory_gib": round(props.total_memory / 2**30, 1)}
     if ext is not None:
         out["extended_reduce"] = ext
     out["roofline"]["step_ms_median"] = step_ms[len(step_ms) // 2]
