@@ -58,10 +58,13 @@
  *     (MISALIGNED), dtype (UNSUPPORTED), overlap of inputs with outputs
  *     (ALIAS), and finally that every array range lies inside one device
  *     allocation (NOT_DEVICE, via hipMemGetAddressRange).  The chunk
- *     table's dst addresses live in device memory and are not checked: they
- *     must come from zero_build_chunks over live parameter buffers, and a
- *     table names each shard element at most once (tables from
- *     zero_build_chunks, and contiguous runs of their chunks, do).
+ *     table lives in device memory, so the step calls cannot read its dst
+ *     addresses without a device round trip; zero_check_chunks checks a
+ *     host table against the arrays of a step once, before the table is
+ *     used (INVALID for a malformed table, ALIAS for a dst range that
+ *     overlaps a partial, a state array or another chunk's dst).  A table
+ *     names each shard element at most once (tables from zero_build_chunks,
+ *     and contiguous runs of their chunks, do).
  *   - `gdt` arguments are plain ints holding a zero_dtype value; any other
  *     value is UNSUPPORTED (the library converts to the enum only after the
  *     check).
@@ -137,7 +140,14 @@ enum {
 
 #define ZERO_MAX_RANKS 64
 #define ZERO_MAX_LEN (((int64_t)1) << 48)   /* largest element or byte count */
-#define ZERO_DEFAULT_MAX_CHUNK 2048   /* chunk length the step kernel is tuned for */
+/* Chunk lengths the step kernels are tuned for: 4 KiB of each partial per
+ * chunk, i.e. 256 lane groups, four passes of a 64-lane wave, with either
+ * partial dtype.  Measured on MI355X in one process on the same buffers:
+ * bf16 partials (7B shard, N = 8) 0.727 of HBM peak with 2048 against 0.701
+ * with 1024 and 0.673 with 4096; fp32 partials (ragged shard, N = 32) 0.677
+ * with 1024 against 0.651 with 2048 and 0.633 with 8192. */
+#define ZERO_DEFAULT_MAX_CHUNK 2048        /* bf16 partials */
+#define ZERO_DEFAULT_MAX_CHUNK_FP32 1024   /* fp32 partials */
 /* Launches of the 16-byte, 12-byte and extended steps (with their bucket
  * and scheduled forms) over at most this many chunks run at a higher
  * occupancy, which suits small shards and single gradient buckets.  Results
@@ -176,7 +186,39 @@ int zero_build_chunks(const int64_t *numels, int n_tensors, int n_ranks, int ran
                       zero_chunk *out, int64_t cap, int64_t *n_out, int64_t *shard_len_out);
 
 /*
+ * Check a chunk table against the arrays of the step that will use it
+ * (host only; no device calls, nothing dereferenced on the device).
+ *
+ * The parameter all-gather writes each shard element's bf16 value into its
+ * slot of the full parameter buffer ("CS336 2026 Lecture 8: Parallelism
+ * Basics", Slide 20, fourth step); a slot must therefore be written once
+ * and must not be an input of the same step.
+ *
+ * chunks:      host copy of the table (n_chunks entries).
+ * shard_len:   the step's shard length.
+ * arrays, array_bytes: n_arrays byte ranges [arrays[i], arrays[i] +
+ *              array_bytes[i]) that the step reads or writes besides the
+ *              destinations: the partials, master, m, v (or comp, m, v),
+ *              an accumulator.  Host arrays of device addresses and sizes.
+ * Returns INVALID for a null or negative argument, a chunk with len < 1,
+ * a null dst, a chunk outside [0, shard_len), or two chunks covering the
+ * same shard element; then ALIAS when two chunks' destinations
+ * [dst, dst + 2 len) overlap, or a destination overlaps one of the arrays.
+ * O(n_chunks log n_chunks) time and O(n_chunks) host memory.
+ */
+int zero_check_chunks(const zero_chunk *chunks, int64_t n_chunks, int64_t shard_len,
+                      const void *const *arrays, const int64_t *array_bytes, int n_arrays);
+
+/*
  * The fused shard step: reduce + AdamW + bf16 write in one pass.
+ *
+ * Defined by the ZeRO lifecycle of "CS336 2026 Lecture 8: Parallelism
+ * Basics", Slides 19-20: gradients are reduce-scattered to the rank that
+ * owns each segment, the owner updates its segment with its own optimizer
+ * state, and the updated parameters are all-gathered; "并行训练优化、MoE扩展与
+ * 系统瓶颈", 2.2.1, gives the same per-rank update of a parameter shard from
+ * its gradient shard and optimizer-state shard.  This call is the local
+ * arithmetic of those three phases for one rank.
  *
  * partials:  host array of n_ranks device pointers; partials[k] holds rank
  *            k's gradient for this shard, shard_len elements of type gdt,
@@ -214,7 +256,10 @@ int zero_shard_step(const void *const *partials, int n_ranks, int gdt,
  * zero_shard_step over the buckets' chunks, bit for bit.  Errors as
  * zero_shard_step; every non-NULL event is probed with hipEventQuery
  * before anything is enqueued, and an invalid one gives HIP with nothing
- * launched.
+ * launched.  Unlike the other calls, this one enqueues several launches:
+ * if the runtime reports an error at the wait or launch of bucket b (not
+ * expected once the checks have passed), buckets before b are already
+ * enqueued and will run, and HIP is returned.
  */
 int zero_shard_step_buckets(const void *const *partials, int n_ranks, int gdt,
                             float *master, float *m, float *v, int64_t shard_len,
@@ -376,6 +421,12 @@ int zero_step_index_advance(int64_t *index, int64_t n_consts, hipStream_t stream
  * Reduce only: grad_out[i] = fp32((p_0[i] + ... + p_{N-1}[i]) / N),
  * i in [0, n), summed in double in rank order.  grad_out must not overlap
  * any partial (ALIAS).  n == 0 is a no-op.
+ *
+ * The local arithmetic of the gradient reduce-scatter: "CS336 2026 Lecture
+ * 8: Parallelism Basics", Slide 8 (all-reduce = reduce-scatter +
+ * all-gather), and "并行策略总览：六个维度各切什么、怎么通信", data-parallel
+ * section (the full-batch gradient is the mean of the ranks' gradients,
+ * because the loss is a sum over samples).
  */
 int zero_reduce_shard(const void *const *partials, int n_ranks, int gdt, int64_t n,
                       float *grad_out, hipStream_t stream);
@@ -384,6 +435,12 @@ int zero_reduce_shard(const void *const *partials, int n_ranks, int gdt, int64_t
  * AdamW only, from an fp32 gradient: master, m, v (n elements each) are
  * updated in place exactly as in zero_shard_step.  grad must not overlap
  * master, m or v (ALIAS).  n == 0 is a no-op.
+ *
+ * The optimizer state is the fp32 master copy and Adam's two moments of
+ * "CS336 2026 Lecture 8: Parallelism Basics", Slide 17 (the
+ * 16-bytes-per-parameter ledger); the pages name the state but not the
+ * update, which is read as decoupled-weight-decay AdamW with bias
+ * correction (the formula in the file comment above).
  */
 int zero_adamw_shard(const float *grad, float *master, float *m, float *v, int64_t n,
                      const zero_adamw_hparams *hp, hipStream_t stream);
@@ -392,6 +449,10 @@ int zero_adamw_shard(const float *grad, float *master, float *m, float *v, int64
  * bf16 write only: for every chunk c and j < c.len,
  * c.dst[j] = bf16(master[c.shard_off + j]).  master holds shard_len fp32
  * elements; chunks outside [0, shard_len) are skipped.
+ *
+ * The local half of the parameter all-gather: "CS336 2026 Lecture 8:
+ * Parallelism Basics", Slide 20, fourth step (each rank's updated segment
+ * goes back into the full bf16 parameters).
  */
 int zero_gather_write(const float *master, int64_t shard_len, const zero_chunk *d_chunks,
                       int64_t n_chunks, hipStream_t stream);

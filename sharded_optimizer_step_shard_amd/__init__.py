@@ -28,7 +28,8 @@ ZERO_OK, ZERO_ERR_INVALID, ZERO_ERR_MISALIGNED, ZERO_ERR_UNSUPPORTED = 0, 1, 2, 
 ZERO_ERR_ALIAS, ZERO_ERR_HIP, ZERO_ERR_CAPACITY, ZERO_ERR_NOT_DEVICE = 4, 5, 6, 7
 ZERO_MAX_RANKS = 64
 ZERO_MAX_LEN = 1 << 48          # largest element or byte count an entry point accepts
-ZERO_DEFAULT_MAX_CHUNK = 2048
+ZERO_DEFAULT_MAX_CHUNK = 2048        # bf16 partials
+ZERO_DEFAULT_MAX_CHUNK_FP32 = 1024   # fp32 partials
 ZERO_SMALL_LAUNCH_CHUNKS = 16384  # step launches up to this many chunks run at a higher occupancy
 
 # Mirrors `zero_chunk` (32 bytes).
@@ -98,6 +99,7 @@ _lib.zero_shard_step_scheduled.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _i64,
 _lib.zero_shard_step_bf16_moments_scheduled.argtypes = _lib.zero_shard_step_scheduled.argtypes
 _lib.zero_shard_step_kahan_scheduled.argtypes = _lib.zero_shard_step_scheduled.argtypes
 _lib.zero_step_index_advance.argtypes = [_vp, _i64, _vp]
+_lib.zero_check_chunks.argtypes = [_vp, _i64, _i64, _vp, _vp, _i32]
 _lib.zero_strerror.argtypes = [_i32]
 _lib.zero_strerror.restype = ctypes.c_char_p
 for _f in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_adamw_shard",
@@ -106,7 +108,7 @@ for _f in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_ad
            "zero_accumulate_shard", "zero_shard_step_bf16_moments", "zero_shard_step_kahan",
            "zero_shard_step_buckets", "zero_make_step_consts", "zero_shard_step_scheduled",
            "zero_step_index_advance", "zero_shard_step_bf16_moments_scheduled",
-           "zero_shard_step_kahan_scheduled"):
+           "zero_shard_step_kahan_scheduled", "zero_check_chunks"):
     getattr(_lib, _f).restype = _i32
 
 Ptr = Union[int, "torch.Tensor", None]  # noqa: F821
@@ -183,6 +185,27 @@ def zero_build_chunks(numels: Sequence[int], n_ranks: int, rank: int,
                                       _addr(slot_dst), max_chunk, out.ctypes.data, n.value,
                                       ctypes.byref(n), ctypes.byref(S)), "zero_build_chunks")
     return out, S.value
+
+
+def _byte_range(x) -> Tuple[int, int]:
+    """(device address, byte count) of a tensor, or an (address, bytes) pair."""
+    if isinstance(x, tuple):
+        return int(x[0]), int(x[1])
+    return _addr(x), x.numel() * x.element_size()
+
+
+def zero_check_chunks(table: np.ndarray, shard_len: int, arrays: Sequence) -> None:
+    """Check a host chunk table against the arrays a step reads or writes
+    besides the destinations (tensors or (address, bytes) pairs): raises
+    ZeroShardError with INVALID for a malformed table, ALIAS when a
+    destination overlaps one of the arrays or another chunk's destination.
+    Host only; call it once per table and set of step arrays."""
+    tab = np.ascontiguousarray(table, dtype=CHUNK_DTYPE)
+    rng = [_byte_range(a) for a in arrays]
+    ptrs = (ctypes.c_void_p * max(len(rng), 1))(*[r[0] for r in rng])
+    sizes = (ctypes.c_int64 * max(len(rng), 1))(*[r[1] for r in rng])
+    _check(_lib.zero_check_chunks(tab.ctypes.data if len(tab) else None, len(tab), shard_len,
+                                  ptrs, sizes, len(rng)), "zero_check_chunks")
 
 
 def chunks_to_device(table: np.ndarray, device: str = "cuda"):

@@ -344,6 +344,9 @@ int zero_shard_step_buckets(const void *const *partials, int n_ranks, int gdt,
                 return ZERO_ERR_HIP;
             }
         }
+        // hipErrorNotReady is an answer, not a failure: clear it so that the
+        // launches' own status check below sees only their errors
+        (void)hipGetLastError();
     }
     for (int b = 0; b < n_buckets; ++b) {
         if (count[b] == 0)

@@ -6,6 +6,10 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+#include <utility>
+#include <vector>
+
 #include "zero_internal.h"
 
 extern "C" {
@@ -82,6 +86,68 @@ int zero_build_chunks(const int64_t *numels, int n_tensors, int n_ranks, int ran
         *shard_len_out = S;
     if (out && count > cap)
         return ZERO_ERR_CAPACITY;
+    return ZERO_OK;
+}
+
+int zero_check_chunks(const zero_chunk *chunks, int64_t n_chunks, int64_t shard_len,
+                      const void *const *arrays, const int64_t *array_bytes, int n_arrays)
+{
+    if (n_chunks < 0 || n_chunks > INT32_MAX || (n_chunks > 0 && !chunks) || shard_len < 0 ||
+        shard_len > ZERO_MAX_LEN || n_arrays < 0 || (n_arrays > 0 && (!arrays || !array_bytes)))
+        return ZERO_ERR_INVALID;
+    for (int i = 0; i < n_arrays; ++i)
+        if (array_bytes[i] < 0 || array_bytes[i] > ZERO_MAX_LEN || (!arrays[i] && array_bytes[i] > 0))
+            return ZERO_ERR_INVALID;
+    typedef std::pair<uintptr_t, uintptr_t> Range;   // [first, second)
+    std::vector<Range> elems, dsts;
+    elems.reserve((size_t)n_chunks);
+    dsts.reserve((size_t)n_chunks);
+    for (int64_t i = 0; i < n_chunks; ++i) {
+        const zero_chunk &c = chunks[i];
+        if (c.len < 1 || c.shard_off < 0 || c.shard_off > shard_len - c.len || !c.dst)
+            return ZERO_ERR_INVALID;
+        const uintptr_t d = (uintptr_t)c.dst, nb = 2 * (uintptr_t)c.len;
+        if (d > UINTPTR_MAX - nb)
+            return ZERO_ERR_INVALID;
+        elems.emplace_back((uintptr_t)c.shard_off, (uintptr_t)(c.shard_off + c.len));
+        dsts.emplace_back(d, d + nb);
+    }
+    // every shard element in at most one chunk
+    std::sort(elems.begin(), elems.end());
+    for (size_t i = 1; i < elems.size(); ++i)
+        if (elems[i].first < elems[i - 1].second)
+            return ZERO_ERR_INVALID;
+    // no two chunks write the same parameter byte
+    std::sort(dsts.begin(), dsts.end());
+    for (size_t i = 1; i < dsts.size(); ++i)
+        if (dsts[i].first < dsts[i - 1].second)
+            return ZERO_ERR_ALIAS;
+    // no destination inside an array the step reads or writes: merge the
+    // arrays into disjoint sorted ranges, then look each destination up
+    std::vector<Range> arr;
+    for (int i = 0; i < n_arrays; ++i) {
+        const uintptr_t a = (uintptr_t)arrays[i], nb = (uintptr_t)array_bytes[i];
+        if (nb == 0)
+            continue;
+        if (a > UINTPTR_MAX - nb)
+            return ZERO_ERR_INVALID;
+        arr.emplace_back(a, a + nb);
+    }
+    std::sort(arr.begin(), arr.end());
+    std::vector<Range> merged;
+    for (const Range &r : arr) {
+        if (!merged.empty() && r.first <= merged.back().second)
+            merged.back().second = std::max(merged.back().second, r.second);
+        else
+            merged.push_back(r);
+    }
+    for (const Range &d : dsts) {
+        // first merged range ending after d starts
+        auto it = std::upper_bound(merged.begin(), merged.end(), d.first,
+                                   [](uintptr_t x, const Range &r) { return x < r.second; });
+        if (it != merged.end() && it->first < d.second)
+            return ZERO_ERR_ALIAS;
+    }
     return ZERO_OK;
 }
 

@@ -100,6 +100,20 @@ int main(int argc, char **argv)
     CHECK_HIP(hipMemcpy(d_v, h_v, (size_t)n * mom, hipMemcpyHostToDevice));
     CHECK_HIP(hipMemcpy(d_table, table, sizeof(zero_chunk) * n_chunks, hipMemcpyHostToDevice));
     CHECK_HIP(hipMemset(d_params, 0xFF, (size_t)total * 2));
+    {   /* the table against every array the step reads or writes */
+        const void **arr = malloc(sizeof(void *) * (n_ranks + 3));
+        int64_t *bytes = malloc(sizeof(int64_t) * (n_ranks + 3));
+        for (int k = 0; k < n_ranks; ++k) {
+            arr[k] = parts[k];
+            bytes[k] = n * 2;
+        }
+        arr[n_ranks] = d_master, bytes[n_ranks] = n * 4;
+        arr[n_ranks + 1] = d_m, bytes[n_ranks + 1] = n * (int64_t)mom;
+        arr[n_ranks + 2] = d_v, bytes[n_ranks + 2] = n * (int64_t)mom;
+        CHECK_ZS(zero_check_chunks(table, n_chunks, n, (const void *const *)arr, bytes, n_ranks + 3));
+        free(arr);
+        free(bytes);
+    }
 
     zero_adamw_hparams hp = {hpd[0], hpd[1], hpd[2], hpd[3], hpd[4], step};
     if (state == 0) {

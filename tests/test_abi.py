@@ -56,6 +56,14 @@ def test_version_and_strerror(zs):
     assert zs.zero_strerror(99) == "unknown error code"
 
 
+def test_header_constants_match_the_binding(zs):
+    text = open(HEADER).read()
+    for name in ("ZERO_MAX_RANKS", "ZERO_DEFAULT_MAX_CHUNK", "ZERO_DEFAULT_MAX_CHUNK_FP32",
+                 "ZERO_SMALL_LAUNCH_CHUNKS"):
+        m = re.search(rf"#define {name}\s+(\d+)", text)
+        assert m and int(m.group(1)) == getattr(zs, name), name
+
+
 def test_struct_layouts(zs):
     assert zs.CHUNK_DTYPE.itemsize == 32
     assert [zs.CHUNK_DTYPE.fields[f][1] for f in ("shard_off", "dst", "len", "tensor_id", "tensor_off")] \
@@ -278,6 +286,81 @@ def test_chunk_table_errors(zs):
     assert call(big.ctypes.data, 1, 1, 0, None, BASE, 64, out.ctypes.data, 4, ctypes.byref(n),
                 None) == zs.ZERO_ERR_CAPACITY
     assert n.value == 16 and out["len"][3] == 64
+
+
+def check(zs, table, shard_len, arrays):
+    """zero_check_chunks through the raw ABI: its return code."""
+    tab = np.ascontiguousarray(table, dtype=zs.CHUNK_DTYPE)
+    ptrs = (ctypes.c_void_p * max(len(arrays), 1))(*[a for a, _ in arrays])
+    sizes = (ctypes.c_int64 * max(len(arrays), 1))(*[b for _, b in arrays])
+    return zs.raw_call("zero_check_chunks", tab.ctypes.data if len(tab) else None, len(tab),
+                       shard_len, ptrs, sizes, len(arrays))
+
+
+def step_arrays(n_ranks, n, gbytes=2, base=BASE):
+    """Byte ranges of a step's partials and fp32 master, m, v (fake addresses)."""
+    parts_ = [(base + k * (1 << 30), n * gbytes) for k in range(n_ranks)]
+    state = [(base + (1 << 40) + i * (1 << 32), n * 4) for i in range(3)]
+    return parts_ + state
+
+
+@pytest.mark.parametrize("mode", ["tensors", "slot"])
+def test_check_chunks_accepts_built_tables(zs, mode):
+    numels = [1000, 7, 4093, 64, 2900]
+    for n_ranks in (1, 3, 4):
+        for rank in range(n_ranks):
+            kw = ({"tensor_dst": [BASE + (1 << 42) + (t << 24) for t in range(len(numels))]}
+                  if mode == "tensors" else {"slot_dst": BASE + (1 << 42)})
+            table, S = zs.zero_build_chunks(numels, n_ranks, rank, max_chunk=128, **kw)
+            n = min(S, sum(numels) - rank * S)
+            assert check(zs, table, n, step_arrays(n_ranks, n)) == zs.ZERO_OK
+            zs.zero_check_chunks(table, n, step_arrays(n_ranks, n))     # binding: no raise
+            # any contiguous run of chunks (a bucket) is valid too
+            assert check(zs, table[1:-1], n, step_arrays(n_ranks, n)) == zs.ZERO_OK
+
+
+def test_check_chunks_alias_and_invalid(zs):
+    """A destination inside m, inside a partial, or shared by two chunks is
+    ALIAS; a malformed table is INVALID (checked first)."""
+    n_ranks, n = 4, 1000
+    arrays = step_arrays(n_ranks, n)
+    slot = BASE + (1 << 42)
+    table, S = zs.zero_build_chunks([n * n_ranks], n_ranks, 0, slot_dst=slot, max_chunk=256)
+    assert S == n and check(zs, table, n, arrays) == zs.ZERO_OK
+    m_base = arrays[n_ranks + 1][0]
+    # dst overlapping m (the last byte of a chunk's range lands on m's first byte)
+    t = table.copy()
+    t["dst"][2] = m_base - 2 * int(t["len"][2]) + 1
+    assert check(zs, t, n, arrays) == zs.ZERO_ERR_ALIAS
+    with pytest.raises(zs.ZeroShardError) as e:
+        zs.zero_check_chunks(t, n, arrays)
+    assert e.value.code == zs.ZERO_ERR_ALIAS
+    # ending exactly where m starts is fine
+    t["dst"][2] = m_base - 2 * int(t["len"][2])
+    assert check(zs, t, n, arrays) == zs.ZERO_OK
+    # dst inside a partial
+    t = table.copy()
+    t["dst"][0] = arrays[3][0] + 16
+    assert check(zs, t, n, arrays) == zs.ZERO_ERR_ALIAS
+    # two chunks writing the same parameters
+    t = table.copy()
+    t["dst"][1] = t["dst"][0] + 2
+    assert check(zs, t, n, arrays) == zs.ZERO_ERR_ALIAS
+    # malformed tables
+    for field, value in (("len", 0), ("shard_off", -1), ("shard_off", n - 10), ("dst", 0)):
+        t = table.copy()
+        t[field][1] = value
+        assert check(zs, t, n, arrays) == zs.ZERO_ERR_INVALID, (field, value)
+    t = table.copy()
+    t["shard_off"][2] = t["shard_off"][1] + 1          # two chunks cover the same element
+    assert check(zs, t, n, arrays) == zs.ZERO_ERR_INVALID
+    # INVALID wins over ALIAS
+    t["dst"][0] = m_base
+    assert check(zs, t, n, arrays) == zs.ZERO_ERR_INVALID
+    assert check(zs, table, n, [(arrays[0][0], -1)]) == zs.ZERO_ERR_INVALID
+    assert check(zs, table, -1, arrays) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_check_chunks", None, 3, n, None, None, 0) == zs.ZERO_ERR_INVALID
+    assert zs.raw_call("zero_check_chunks", None, 0, n, None, None, 0) == zs.ZERO_OK
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

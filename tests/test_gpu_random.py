@@ -110,6 +110,7 @@ def test_random_case(zs, seed):
                                          max_chunk=c["max_chunk"])
         read_params = lambda: np.concatenate([host(b) for b in bufs])    # noqa: E731
     assert S2 == S
+    zs.zero_check_chunks(table, n, parts)     # every built table passes the host check
     d_table, nc = zs.chunks_to_device(table), len(table)
     layout = c["layout"]
 
