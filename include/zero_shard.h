@@ -148,11 +148,13 @@ enum {
  * with 1024 against 0.651 with 2048 and 0.633 with 8192. */
 #define ZERO_DEFAULT_MAX_CHUNK 2048        /* bf16 partials */
 #define ZERO_DEFAULT_MAX_CHUNK_FP32 1024   /* fp32 partials */
-/* Launches of the 16-byte, 12-byte and extended steps (with their bucket
- * and scheduled forms) over at most this many chunks run at a higher
- * occupancy, which suits small shards and single gradient buckets.  Results
- * are the same bits either way. */
-#define ZERO_SMALL_LAUNCH_CHUNKS 16384
+/* Launches over at most this many chunks run at a higher occupancy, which
+ * suits small shards and single gradient buckets: ZERO_SMALL_LAUNCH_CHUNKS
+ * for the 16-byte and extended steps (with their bucket and scheduled
+ * forms), ZERO_SMALL_LAUNCH_CHUNKS_12B for the 12-byte step.  Results are
+ * the same bits either way. */
+#define ZERO_SMALL_LAUNCH_CHUNKS 2048
+#define ZERO_SMALL_LAUNCH_CHUNKS_12B 16384
 
 /*
  * Shard geometry and the chunk table (host only; no device calls).

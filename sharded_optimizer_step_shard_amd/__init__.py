@@ -30,7 +30,9 @@ ZERO_MAX_RANKS = 64
 ZERO_MAX_LEN = 1 << 48          # largest element or byte count an entry point accepts
 ZERO_DEFAULT_MAX_CHUNK = 2048        # bf16 partials
 ZERO_DEFAULT_MAX_CHUNK_FP32 = 1024   # fp32 partials
-ZERO_SMALL_LAUNCH_CHUNKS = 16384  # step launches up to this many chunks run at a higher occupancy
+# step launches up to this many chunks run at a higher occupancy
+ZERO_SMALL_LAUNCH_CHUNKS = 2048        # 16-byte and extended steps
+ZERO_SMALL_LAUNCH_CHUNKS_12B = 16384   # 12-byte step
 
 # Mirrors `zero_chunk` (32 bytes).
 CHUNK_DTYPE = np.dtype([("shard_off", "<i8"), ("dst", "<u8"), ("len", "<i4"),

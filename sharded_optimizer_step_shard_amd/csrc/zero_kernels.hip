@@ -514,13 +514,16 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
 // (0.725 against 0.69), the pure-bf16 step with two (0.63 -> 0.71; its
 // registers allow no third).
 //
-// SMALL: a launch of at most ZERO_SMALL_LAUNCH_CHUNKS chunks, where the
+// SMALL: a launch of at most ZERO_SMALL_LAUNCH_CHUNKS_12B chunks, where the
 // launch's ramp and tail weigh more; there the 12-byte step with few
-// partials runs three waves with batches of 8.  Measured (N = 8 bf16,
-// chunks of 2048, one process, two waves / three): 4M-element shards
-// 0.51-0.52 / 0.56-0.59, 16M 0.55-0.63 / 0.69-0.71, 32M 0.61-0.64 /
-// 0.69-0.79, 128M and 256M 0.64-0.69 / 0.67-0.68.  The pure-bf16 step gained
-// nothing from two or four waves on the GPT-2 shard.
+// partials runs three waves with batches of 8.  Measured with each launch on
+// the next of enough buffer sets to keep the working set (over 2 GB) out of
+// the 256 MB last-level cache (N = 8 bf16, chunks of 2048, one process, two
+// waves / three): 2M-element shards 0.39 / 0.41-0.43, 4M 0.45-0.48 /
+// 0.48-0.51, 8M 0.51-0.55 / 0.53-0.56, 16M 0.55-0.60 / 0.60-0.61, 32M
+// 0.59-0.64 / 0.64-0.65; 128M and 256M (one buffer set) 0.64-0.69 /
+// 0.67-0.68.  The pure-bf16 step gained nothing from two or four waves on
+// the GPT-2 shard.
 template <zero_dtype G, int NC, bool SMALL>
 constexpr int kM16Waves = (NC > 0 && NC * Grad<G>::BYTES <= 16) ? (SMALL ? 3 : 2) : 1;
 constexpr int kKahanWaves = 3;
@@ -674,9 +677,21 @@ void shard_step_m16_kernel(StepArgs a)
 // chunks (a small shard, or one gradient bucket) runs two: with few
 // workgroups per CU the launch's ramp and tail weigh more than the
 // read/write mix.  Measured on MI355X, N = 8 bf16, chunks of 2048, one
-// process: 4M-element shards 0.54-0.57 of HBM peak with one wave against
-// 0.64-0.67 with two, 16M 0.65-0.69 against 0.74-0.77, 32M about even,
-// 128M and more 0.69-0.72 against 0.67.
+// process, each launch on the next of enough buffer sets to keep the
+// working set (over 2 GB) out of the 256 MB last-level cache, one wave
+// against two: 2M-element shards 0.45 / 0.44-0.45, 4M 0.49-0.50 /
+// 0.51-0.52, 8M 0.58 / 0.57-0.58, 16M 0.62-0.64 / 0.60, 32M 0.68-0.70 /
+// 0.67, 64M 0.70-0.71 / 0.68; 7B gradient buckets of 4M params (2048
+// chunks) 0.547 / 0.568, of 16M (8192 chunks) 0.662 / 0.652.  (Re-stepping
+// one buffer set instead favours two waves up to 16M elements, 0.79 against
+// 0.71 there, because part of the set then stays in that cache.)
+//
+// The allocation behind one wave per SIMD: with amdgpu_waves_per_eu(1, 1)
+// the compiler declares 257 registers (.amdhsa_next_free_vgpr; 114 of them
+// used), and 257 rounded to gfx950's granule of 8 fills more than half of
+// a SIMD's 512, so only one such wave fits.  The two-wave instance declares
+// 169 (176 allocated, two fit).  rocprofv3 reports the 257 as "132" (it
+// counts granules of 4).
 template <zero_dtype G, int NC, bool EXT, int KC = -1, int W = 1>
 __global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, W)))
 void shard_step_kernel(StepArgs a)
@@ -926,7 +941,7 @@ static hipError_t step_sched_dispatch(const StepArgs &a, hipStream_t s)
 template <int L>
 static hipError_t step_sched_layout(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 {
-    const bool small = a.n_chunks <= ZERO_SMALL_LAUNCH_CHUNKS;
+    const bool small = a.n_chunks <= (L == 1 ? ZERO_SMALL_LAUNCH_CHUNKS_12B : ZERO_SMALL_LAUNCH_CHUNKS);
     if (gdt == ZERO_BF16)
         return small ? step_sched_dispatch<L, ZERO_BF16, true>(a, s)
                      : step_sched_dispatch<L, ZERO_BF16, false>(a, s);
@@ -1033,7 +1048,7 @@ hipError_t launch_step_kahan(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 
 hipError_t launch_step_m16(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 {
-    const bool small = a.n_chunks <= ZERO_SMALL_LAUNCH_CHUNKS;
+    const bool small = a.n_chunks <= ZERO_SMALL_LAUNCH_CHUNKS_12B;
     if (gdt == ZERO_BF16)
         return small ? step_m16_dispatch<ZERO_BF16, true>(a, s) : step_m16_dispatch<ZERO_BF16, false>(a, s);
     return small ? step_m16_dispatch<ZERO_FP32, true>(a, s) : step_m16_dispatch<ZERO_FP32, false>(a, s);
@@ -1042,9 +1057,11 @@ hipError_t launch_step_m16(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 hipError_t launch_step_ex(const StepArgs &a, zero_dtype gdt, hipStream_t s)
 {
     // the same occupancy rule as the 16-byte step (same structure); measured
-    // with one accumulated micro-batch, N = 8 bf16: 4M-element shards 0.54 ->
-    // 0.64-0.65 of the plain step's bytes per second, 16M 0.57-0.64 ->
-    // 0.68-0.72, 256M 0.65-0.66 with one wave against 0.61 with two
+    // with one accumulated micro-batch, N = 8 bf16, working set kept out of
+    // the last-level cache as for the 16-byte step, one wave against two:
+    // 2M-element shards 0.44 / 0.45, 4M 0.47 / 0.48, 8M 0.54-0.55 / 0.53-0.54,
+    // 16M 0.60-0.64 / 0.63, 32M 0.65-0.68 / 0.66-0.67 of the bytes of the
+    // step with its accumulator read; 256M 0.65-0.66 / 0.61
     const bool small = a.n_chunks <= ZERO_SMALL_LAUNCH_CHUNKS;
     if (gdt == ZERO_BF16)
         return small ? step_ex_dispatch<ZERO_BF16, 2>(a, s) : step_ex_dispatch<ZERO_BF16, 1>(a, s);

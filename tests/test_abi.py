@@ -59,7 +59,7 @@ def test_version_and_strerror(zs):
 def test_header_constants_match_the_binding(zs):
     text = open(HEADER).read()
     for name in ("ZERO_MAX_RANKS", "ZERO_DEFAULT_MAX_CHUNK", "ZERO_DEFAULT_MAX_CHUNK_FP32",
-                 "ZERO_SMALL_LAUNCH_CHUNKS"):
+                 "ZERO_SMALL_LAUNCH_CHUNKS", "ZERO_SMALL_LAUNCH_CHUNKS_12B"):
         m = re.search(rf"#define {name}\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(zs, name), name
 

@@ -10,11 +10,11 @@ the dispatcher distinguishes for that N (flat, compiled 4, compiled 8, a
 group size folded at run time), each with one accumulated micro-batch.
 
 The 16-byte, 12-byte and extended steps also compile two occupancies
-each: launches of at most ZERO_SMALL_LAUNCH_CHUNKS chunks run more waves
-per SIMD than longer ones.  The small cases take the first; a second case
-per (dtype, N) builds a table just over that many chunks to take the other,
-for the launch-argument and scheduled forms and every fold of the
-extended step.
+each: launches of at most ZERO_SMALL_LAUNCH_CHUNKS chunks (the 12-byte
+step: ZERO_SMALL_LAUNCH_CHUNKS_12B) run more waves per SIMD than longer
+ones.  The small cases take the first; a second case per (dtype, N) builds
+a table just over the larger limit to take the other, for the
+launch-argument and scheduled forms and every fold of the extended step.
 """
 import numpy as np
 import pytest
@@ -137,14 +137,15 @@ def test_every_compiled_variant(zs, gdt, n_ranks):
 @pytest.mark.parametrize("gdt", ["bf16", "f32"])
 @pytest.mark.parametrize("n_ranks", RANKS)
 def test_large_launch_variants_over_a_long_table(zs, gdt, n_ranks):
-    n = zs.ZERO_SMALL_LAUNCH_CHUNKS * 64 + 777      # chunks of 64: just over the limit
+    limit = max(zs.ZERO_SMALL_LAUNCH_CHUNKS, zs.ZERO_SMALL_LAUNCH_CHUNKS_12B)
+    n = limit * 64 + 777                             # chunks of 64: just over both limits
     w = W.Workload("variants-long", 97, [n * n_ranks], n_ranks, gdt, 1e-3)
     lo, hi = w.shard_range(0)
     assert hi - lo == n
     idx = np.arange(lo, hi, dtype=np.int64)
     slot = torch.full((n,), -1, dtype=torch.int16, device="cuda")
     table, _ = zs.zero_build_chunks([n * n_ranks], n_ranks, 0, slot_dst=slot, max_chunk=64)
-    assert len(table) > zs.ZERO_SMALL_LAUNCH_CHUNKS
+    assert len(table) > limit
     d_table, nc = zs.chunks_to_device(table), len(table)
     t = 3
     parts_h = host_partials(w, t, idx)
