@@ -1,6 +1,7 @@
 """Benchmark of the fused ZeRO shard step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama7b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama70b]
+                    [--secondary llama7b] [--allocations 3]
 
 A step is one call of zero_shard_step: reduce the N gradient partials of
 this rank's shard, AdamW on the shard's fp32 master/m/v, write the bf16
@@ -8,10 +9,13 @@ parameters into their slots.  Inputs are synthetic, seeded, and resident
 in HBM before timing starts.  The partials are the same for every timed
 step (one batch); the optimizer state advances.
 
-Prints one JSON line: params/s over the shard, the roofline block of the
-step kernel (algorithmic HBM bytes per launch / measured launch time against
-the 8 TB/s HBM peak), and the CPU oracle timed on a bounded sample of the
-same workload on this host.
+Prints one JSON line: params/s over the shard (the Llama-70B rank-0 shard by
+default, the largest configuration that fits one GPU), the roofline block of
+the step kernel (algorithmic HBM bytes per launch / measured launch time
+against the 8 TB/s HBM peak; the median of several fresh allocations), the
+same record for a secondary workload (the Llama-7B rank-0 shard), plain
+read/write/copy streams of the library and of the vendor's libraries, and the
+CPU oracle timed on a bounded sample of the same workload on this host.
 
 The workload setup below (allocation, device fill, warm start) is also what
 the full-size GPU parity tests run, so they check the configuration timed
@@ -108,7 +112,8 @@ class Shard:
 
         self.w, self.rank, self.zs = w, rank, zs
         self.dst_mode = dst_mode or default_dst_mode(w)
-        max_chunk = max_chunk or zs.ZERO_DEFAULT_MAX_CHUNK
+        max_chunk = max_chunk or (zs.ZERO_DEFAULT_MAX_CHUNK if w.gdt == "bf16"
+                                  else zs.ZERO_DEFAULT_MAX_CHUNK_FP32)
         self.lo, self.hi = w.shard_range(rank)
         self.n = self.hi - self.lo
         self.S = w.shard_len
@@ -130,6 +135,9 @@ class Shard:
         else:
             raise ValueError(self.dst_mode)
         assert S == self.S
+        # once per table: no destination overlaps a partial, the state or
+        # another chunk's destination
+        zs.zero_check_chunks(table, self.n, self.partials + [self.master, self.m, self.v])
         self.table = table
         self.d_table = zs.chunks_to_device(table, dev)
         self.step_t = 0
@@ -378,29 +386,38 @@ def bucket_runs(chunk_lens, bucket_params: int) -> list:
 
 
 def cpu_baseline(w: W.Workload, rank: int, t: int, target_s: float = 10.0,
-                 sample: int = 1 << 22, state: str = "fp32") -> dict:
+                 sample: int = 1 << 30, state: str = "fp32", single_sample: int = 1 << 24) -> dict:
     """The CPU oracle of the same step (the same state layout) on a bounded
-    sample (the first `sample` shard elements) of the same workload,
-    repeated until ~target_s of work; params/s.  Then the same on one
-    thread over a quarter of the sample."""
+    sample (the first `sample` shard elements) of the same workload, on all
+    host threads, repeated until ~target_s of work; params/s.  Then the same
+    on one thread over the first `single_sample` elements."""
     import oracle
 
     lo, hi = w.shard_range(rank)
     n = min(sample, hi - lo)
+    t_gen = time.perf_counter()
     parts = [synth.fill(w.gdt, w.seed, synth.stream_id(synth.KIND_GRAD, k, t), lo, n,
                         w.sigma_grad, synth.stream_id(synth.KIND_OUTLIER, k, t),
                         w.outlier_frac, w.outlier_mult) for k in range(w.n_ranks)]
+    for a, b in W.zero_ranges(w, lo, lo + n):
+        for p in parts:
+            p[a:b] = 0
     master = synth.fill("f32", w.seed, synth.stream_id(synth.KIND_MASTER), lo, n, w.sigma_master)
-    zero16 = np.zeros(n, np.uint16)
+    gen_s = time.perf_counter() - t_gen
 
     def run(k: int, budget: float) -> tuple:
-        """Oracle steps over the first k elements until `budget` seconds."""
+        """Oracle steps over the first k elements until `budget` seconds
+        (at least one step)."""
         sub = [p[:k] for p in parts]
-        th, m, v = master[:k].copy(), np.zeros(k, np.float32), np.zeros(k, np.float32)
-        th16, c16 = oracle.bf16_round(th), zero16[:k].copy()
-        m16, v16 = zero16[:k].copy(), zero16[:k].copy()
+        if state in ("fp32", "unfused"):
+            th, m, v = master[:k].copy(), np.zeros(k, np.float32), np.zeros(k, np.float32)
+        elif state == "bf16-moments":
+            th, m16, v16 = master[:k].copy(), np.zeros(k, np.uint16), np.zeros(k, np.uint16)
+        else:
+            th16, c16 = oracle.bf16_round(master[:k]), np.zeros(k, np.uint16)
+            m16, v16 = np.zeros(k, np.uint16), np.zeros(k, np.uint16)
         done, elapsed, reps = 0, 0.0, 0
-        while elapsed < budget:
+        while elapsed < budget or reps == 0:
             hp = oracle.hparams(t + reps, **w.hparams())
             t0 = time.perf_counter()
             if state in ("fp32", "unfused"):
@@ -416,7 +433,7 @@ def cpu_baseline(w: W.Workload, rank: int, t: int, target_s: float = 10.0,
 
     cores = oracle.max_threads()
     value, reps, elapsed = run(n, target_s)
-    n1 = max(1, n // 4)
+    n1 = max(1, min(n // 4, single_sample))
     oracle.set_threads(1)
     try:
         value1, reps1, elapsed1 = run(n1, target_s / 4)
@@ -427,7 +444,9 @@ def cpu_baseline(w: W.Workload, rank: int, t: int, target_s: float = 10.0,
     return {"value": value, "unit": "params/s", "cores": cores,
             "kind": "oracle",
             "sample": f"first {n} elements of rank {rank}'s shard of {w.name}, N={w.n_ranks} "
-                      f"{w.gdt} partials, {state} state, {reps} oracle steps in {elapsed:.1f} s",
+                      f"{w.gdt} partials, {state} state, {reps} oracle steps in {elapsed:.1f} s "
+                      f"(inputs generated on the host in {gen_s:.1f} s, not timed)",
+            "sample_elements": n,
             "host_gbs": value * bpp / 1e9,
             "single_thread": {"value": value1, "unit": "params/s",
                               "sample": f"first {n1} elements, {reps1} steps in {elapsed1:.1f} s"},
@@ -696,85 +715,10 @@ def trace_summary(kernel_trace_csv: str) -> str:
     return "\n".join(lines)
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama7b", choices=sorted(W.ALL))
-    ap.add_argument("--rank", type=int, default=0)
-    ap.add_argument("--dst", default=None, choices=["slot", "tensors"])
-    ap.add_argument("--max-chunk", type=int, default=None,
-                    help="chunk-table cut length (default: the library's tuned value)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--state", default="fp32", choices=sorted(STATES),
-                    help="optimizer state: fp32 master, m, v (16 B/param ledger); fp32 "
-                         "master with bf16 m, v (12 B/param ledger); or pure bf16 with a "
-                         "Kahan-compensated update (no master, 10 B/param).  'unfused' runs "
-                         "the 16 B/param step as three kernels (reduce, AdamW, bf16 write)")
-    ap.add_argument("--group", type=int, default=0,
-                    help="two-level reduce: ranks per group (hybrid sharding); 0 = flat")
-    ap.add_argument("--micro-batches", type=int, default=1,
-                    help="gradient accumulation: micro-batches per optimizer step")
-    ap.add_argument("--bucket-params", type=int, default=0,
-                    help="step the shard in buckets of about this many params, one launch "
-                         "per bucket (ZeRO-2 bucketed step); 0 = one launch per step")
-    ap.add_argument("--bucket-call", default="one", choices=["one", "per-bucket"],
-                    help="with --bucket-params: enqueue all buckets with one "
-                         "zero_shard_step_buckets call, or call zero_shard_step per bucket")
-    ap.add_argument("--scheduled", action="store_true",
-                    help="take the step constants from a device table (zero_shard_step_"
-                         "scheduled + zero_step_index_advance): with --graph every replay "
-                         "is the next step")
-    ap.add_argument("--graph", action="store_true",
-                    help="capture one step's launches in a HIP graph and time its replays "
-                         "(the hyper-parameters, step t included, are fixed at capture; the "
-                         "work per replay is the step's)")
-    ap.add_argument("--probe-copy", type=int, default=1 << 32, metavar="BYTES",
-                    help="after timing, copy BYTES with the library's plain copy kernel "
-                         "(measured copy bandwidth of this GPU; the known-size kernel that "
-                         "calibrates HBM traffic counters); 0 to skip")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="no GPU: turn the counter_collection CSVs of two rocprofv3 passes "
-                         "(--pmc FETCH_SIZE, --pmc WRITE_SIZE) over this same command into "
-                         "calibrated HBM bytes per launch, recorded in profiles/traffic.json")
-    ap.add_argument("--launch-overhead", action="store_true",
-                    help="print the per-call cost of zero_shard_step on a small shard (JSON)")
-    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
-                    help="no GPU: print a markdown table of a rocprofv3 kernel trace")
-    args = ap.parse_args()
-
-    if args.trace_summary:
-        print(trace_summary(args.trace_summary))
-        return 0
-    if args.launch_overhead:
-        print(json.dumps(launch_overhead(max_chunk=args.max_chunk)), flush=True)
-        return 0
-    if args.ingest_counters:
-        rec = ingest_counters(*args.ingest_counters, W.get(args.workload), args.rank, args.state,
-                              args.probe_copy)
-        print(json.dumps(rec, indent=1))
-        return 0
-
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs one rank's shard step on one GPU; "
-                                   "--gpus above 1 is not supported (the collectives that "
-                                   "would feed it are out of scope)"}), flush=True)
-        return 2
-
+def setup_step(sh: Shard, args, t: int):
+    """Select the step of the requested mode on a prepared shard; returns
+    (step function, launches per step, extended?)."""
     import torch
-
-    w = W.get(args.workload)
-    max_chunk = args.max_chunk
-    if max_chunk is None and args.bucket_params > 0:
-        max_chunk = bucket_chunk_len(args.bucket_params)
-    sh = Shard(w, args.rank, args.dst, max_chunk)
-    t = sh.prepare()
-    torch.cuda.synchronize()
-    print(f"# {w.name}: shard {sh.n} params, N={w.n_ranks} {w.gdt}, {len(sh.table)} chunks, "
-          f"dst={sh.dst_mode}, first timed step t={t + args.warmup}", file=sys.stderr, flush=True)
-
     step = sh.step
     extended = args.group > 0 or args.micro_batches > 1
     if extended and args.bucket_params > 0:
@@ -813,6 +757,28 @@ def main() -> int:
                 step(t)
         torch.cuda.current_stream().wait_stream(side)
         step = lambda _t: graph.replay()        # noqa: E731
+    launches = len(sh.buckets) if args.bucket_params > 0 else 1
+    return step, launches, extended
+
+
+def time_allocation(w: W.Workload, args, alloc: int) -> dict:
+    """One fresh allocation of the shard: allocate (behind a spacer whose size
+    differs per allocation, so that the buffers land elsewhere), fill, warm
+    start, W untimed steps, then exactly K timed steps.  Returns the
+    measurement; everything is freed before returning."""
+    import torch
+    # spacer: 0, 1 GiB + 2 MiB, 2 GiB + 4 MiB, ...
+    spacer = torch.empty(alloc * ((1 << 30) + (2 << 20)), dtype=torch.uint8, device="cuda")
+    max_chunk = args.max_chunk
+    if max_chunk is None and args.bucket_params > 0:
+        max_chunk = bucket_chunk_len(args.bucket_params)
+    sh = Shard(w, args.rank, args.dst, max_chunk)
+    t = sh.prepare()
+    torch.cuda.synchronize()
+    print(f"# {w.name} allocation {alloc}: shard {sh.n} params, N={w.n_ranks} {w.gdt}, "
+          f"{len(sh.table)} chunks, dst={sh.dst_mode}, first timed step t={t + args.warmup}",
+          file=sys.stderr, flush=True)
+    step, launches, extended = setup_step(sh, args, t)
     for _ in range(args.warmup):
         step(t)
         t += 1
@@ -829,7 +795,6 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = wall * 1e3 / args.steps
-    launches = len(sh.buckets) if args.bucket_params > 0 else 1
     step_ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps))
     kernel_ms = evs[0].elapsed_time(evs[-1]) / args.steps / launches   # average launch
     ext = None
@@ -851,35 +816,98 @@ def main() -> int:
         kernel_ms = e2.elapsed_time(e3) / args.steps
         ext = {"group": args.group, "micro_batches": args.micro_batches,
                "step_ms_including_accumulation": ms_per_step}
-
     bytes_launch = sh.bytes_per_launch() / launches
     if extended and args.micro_batches > 1:
         bytes_launch += 4 * sh.n           # the accumulator read by the fused launch
-    achieved = bytes_launch / (kernel_ms * 1e-3) / 1e9
+    res = {"alloc": alloc, "n": sh.n, "chunks": len(sh.table), "dst": sh.dst_mode,
+           "max_chunk": int(sh.table["len"].max()) if len(sh.table) else 0,
+           "bytes_per_param": sh.bytes_per_launch() // sh.n, "launches": launches,
+           "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "step_ms": step_ms,
+           "bytes_launch": bytes_launch, "extended": ext, "next_t": t,
+           "achieved": bytes_launch / (kernel_ms * 1e-3) / 1e9}
+    del step, sh, spacer
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def chunk_sweep(w: W.Workload, args, lengths, rounds: int = 3) -> dict:
+    """The plain fused step with chunk tables cut at each of `lengths`, over
+    the same buffers of one allocation, taken round-robin `rounds` times
+    (W untimed and K timed steps per turn): the fraction of HBM peak per
+    chunk length, free of the spread between allocations."""
+    import torch
+    zs_ = __import__("sharded_optimizer_step_shard_amd")
+    sh = Shard(w, args.rank, args.dst, max(lengths))
+    t = sh.prepare()
+    kw = ({"slot_dst": sh.params[0]} if sh.dst_mode == "slot" else {"tensor_dst": sh.params})
+    tables = {}
+    for mc in lengths:
+        table, _ = zs_.zero_build_chunks(w.numels, w.n_ranks, args.rank, max_chunk=mc, **kw)
+        zs_.zero_check_chunks(table, sh.n, sh.partials + [sh.master, sh.m, sh.v])
+        tables[mc] = (zs_.chunks_to_device(table), len(table))
+    stream = torch.cuda.current_stream()
+    res = {mc: [] for mc in lengths}
+    for _ in range(rounds):
+        for mc in lengths:
+            dt, nc = tables[mc]
+
+            def step():
+                nonlocal t
+                zs_.zero_shard_step(sh.partials, sh.master, sh.m, sh.v, sh.n, dt, nc,
+                                    zs_.hparams(t, **w.hparams()))
+                t += 1
+            for _ in range(args.warmup):
+                step()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            res[mc].append(sh.bytes_per_launch() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    return {"workload": f"{w.name} rank-{args.rank} shard", "steps_per_turn": args.steps,
+            "rounds": rounds,
+            "by_max_chunk": {str(mc): {"chunks": tables[mc][1], "frac": fr,
+                                       "median": sorted(fr)[len(fr) // 2]}
+                             for mc, fr in res.items()}}
+
+
+def measure_workload(w: W.Workload, args) -> dict:
+    """The step on `args.allocations` fresh allocations of the shard; the
+    record of the allocation with the median roofline fraction, with the
+    fractions of all of them."""
+    runs = [time_allocation(w, args, a) for a in range(args.allocations)]
+    fr = [r["achieved"] / HBM_PEAK_GBS for r in runs]
+    order = sorted(range(len(runs)), key=lambda i: fr[i])
+    med = runs[order[len(order) // 2]]
+    med["frac_by_allocation"] = {"min": min(fr), "median": fr[order[len(order) // 2]],
+                                 "max": max(fr), "values": fr}
+    return med
+
+
+def workload_record(w: W.Workload, args, r: dict) -> dict:
+    """The metric, config and roofline of one measured workload."""
+    extended = r["extended"] is not None
     kname = "shard_step_sched_kernel" if args.scheduled else STATES[args.state][0]
     kernel_key = f"{kname}<{w.gdt},{w.n_ranks}{',ext' if extended else ''}>/{w.name}"
-    traffic = load_traffic(kernel_key) if launches == 1 else None
+    traffic = load_traffic(kernel_key) if r["launches"] == 1 else None
+    achieved = r["achieved"]
     out = {
-        "metric": "params updated/sec and achieved HBM GB/s (fraction of peak), fused shard step",
-        "value": sh.n / (ms_per_step * 1e-3),
+        "value": r["n"] / (r["ms_per_step"] * 1e-3),
         "unit": "params/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f64",
-        "data": "synthetic",
-        "config": {"workload": f"{w.name} rank-{args.rank} shard", "shard_params": sh.n,
+        "ms_per_step": r["ms_per_step"],
+        "config": {"workload": f"{w.name} rank-{args.rank} shard", "shard_params": r["n"],
                    "n_ranks": w.n_ranks, "grad_dtype": w.gdt,
                    "state_dtype": STATES[args.state][3],
-                   "param_dtype": "bf16", "tensors": len(w.numels), "chunks": len(sh.table),
-                   "dst": sh.dst_mode, "bytes_per_param": sh.bytes_per_launch() // sh.n,
+                   "param_dtype": "bf16", "tensors": len(w.numels), "chunks": r["chunks"],
+                   "dst": r["dst"], "bytes_per_param": r["bytes_per_param"],
                    "state": args.state,
-                   "launches_per_step": launches,
-                   "max_chunk": int(sh.table["len"].max()) if len(sh.table) else 0,
+                   "launches_per_step": r["launches"],
+                   "max_chunk": r["max_chunk"],
                    "graph_replay": bool(args.graph),
                    "scheduled_constants": bool(args.scheduled),
                    "bucket_call": args.bucket_call if args.bucket_params > 0 else None,
@@ -888,34 +916,227 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
-                     "kernel": kernel_key, "kernel_ms": kernel_ms,
-                     "algorithmic_bytes_per_launch": bytes_launch},
+                     "kernel": kernel_key, "kernel_ms": r["kernel_ms"],
+                     "algorithmic_bytes_per_launch": r["bytes_launch"],
+                     "step_ms_median": r["step_ms"][len(r["step_ms"]) // 2],
+                     "step_ms_min": r["step_ms"][0],
+                     "frac_by_allocation": r["frac_by_allocation"]},
     }
+    if extended:
+        out["extended_reduce"] = r["extended"]
+    return out
+
+
+def best_rates(probes: dict, vendor: dict = None) -> tuple:
+    """The highest read-only and write-only rates measured in this run: the
+    library's probes, and the vendor's write-only fill when it was timed."""
+    read = probes["probe_read"]["gbs"]
+    write = probes["probe_write"]["gbs"]
+    if vendor and "torch_fill_" in vendor:
+        write = max(write, vendor["torch_fill_"]["gbs"])
+    return read, write
+
+
+def add_mix_model(rec: dict, w: W.Workload, args, n: int, probes: dict,
+                  vendor: dict = None) -> None:
+    """The step's rate against the same run's plain-stream rates: the copy
+    and read probes, and the serial bound of its own read/write mix from the
+    best read-only and write-only rates of the run."""
+    rl = rec["roofline"]
+    achieved = rl["achieved"]
+    rl["vs_copy_probe"] = achieved / probes["probe_copy"]["gbs"]
+    rl["vs_read_probe"] = achieved / probes["probe_read"]["gbs"]
+    _, rd, wr, _ = STATES[args.state]
+    gb = 2 if w.gdt == "bf16" else 4
+    rb, wb = (w.n_ranks * gb + rd) * n, wr * n
+    if args.micro_batches > 1:
+        rb += 4 * n
+    read, write = best_rates(probes, vendor)
+    bound = mix_bound(rb, wb, read, write)
+    rl["mix_model"] = {"read_bytes": rb, "write_bytes": wb, "read_gbs": read, "write_gbs": write,
+                       "bound_gbs": bound, "frac_of_bound": achieved / bound}
+
+
+def vendor_streams(nbytes: int, probes: dict, reps: int = 10) -> dict:
+    """Element-wise streams of the vendor's libraries (torch's HIP kernels),
+    which this library did not write, on fp32 operands of nbytes each: the
+    2:1 read/write mix of torch.add, the 3:1 mix of torch.addcmul, the 1:1
+    device-to-device copy and the write-only fill.  Each with its rate, its
+    fraction of the 8 TB/s peak and of its own serial read/write bound from
+    the same run's best read-only and write-only rates."""
+    import torch
+    n = nbytes // 4
+    a = torch.full((n,), 1.0, device="cuda")
+    b = torch.full((n,), 2.0, device="cuda")
+    c = torch.empty(n, device="cuda")
+    d = torch.empty(n, device="cuda")
+    cases = {
+        "torch_add_out": (lambda: torch.add(a, b, out=c), 2, 1),
+        "torch_addcmul_out": (lambda: torch.addcmul(a, b, c, out=d), 3, 1),
+        "torch_copy_": (lambda: c.copy_(a), 1, 1),
+        "torch_fill_": (lambda: d.fill_(3.0), 0, 1),
+    }
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, (fn, r, wr) in cases.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        rb, wb = r * 4 * n, wr * 4 * n
+        gbs = (rb + wb) / (ms * 1e-3) / 1e9
+        out[name] = {"read_bytes": rb, "write_bytes": wb, "ms": ms, "gbs": gbs,
+                     "frac_of_peak": gbs / HBM_PEAK_GBS}
+    # bounds from the best read-only and write-only rates, the fill's included
+    rates = best_rates(probes, out)
+    for v in out.values():
+        v["frac_of_mix_bound"] = v["gbs"] / mix_bound(v["read_bytes"], v["write_bytes"], *rates)
+    del a, b, c, d
+    torch.cuda.empty_cache()
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama70b", choices=sorted(W.ALL),
+                    help="the headline workload (default: the Llama-70B rank-0 shard, the "
+                         "largest configuration that fits one GPU)")
+    ap.add_argument("--secondary", default="llama7b", choices=sorted(W.ALL) + ["none"],
+                    help="a second workload measured the same way and nested in the line "
+                         "(default: the Llama-7B rank-0 shard); 'none' to skip")
+    ap.add_argument("--allocations", type=int, default=3,
+                    help="fresh allocations of each shard, each timed for K steps; the line "
+                         "reports the allocation with the median roofline fraction")
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--dst", default=None, choices=["slot", "tensors"])
+    ap.add_argument("--max-chunk", type=int, default=None,
+                    help="chunk-table cut length (default: the library's tuned value)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 30,
+                    help="shard elements the CPU oracle is timed on")
+    ap.add_argument("--no-vendor-streams", action="store_true")
+    ap.add_argument("--state", default="fp32", choices=sorted(STATES),
+                    help="optimizer state: fp32 master, m, v (16 B/param ledger); fp32 "
+                         "master with bf16 m, v (12 B/param ledger); or pure bf16 with a "
+                         "Kahan-compensated update (no master, 10 B/param).  'unfused' runs "
+                         "the 16 B/param step as three kernels (reduce, AdamW, bf16 write)")
+    ap.add_argument("--group", type=int, default=0,
+                    help="two-level reduce: ranks per group (hybrid sharding); 0 = flat")
+    ap.add_argument("--micro-batches", type=int, default=1,
+                    help="gradient accumulation: micro-batches per optimizer step")
+    ap.add_argument("--bucket-params", type=int, default=0,
+                    help="step the shard in buckets of about this many params, one launch "
+                         "per bucket (ZeRO-2 bucketed step); 0 = one launch per step")
+    ap.add_argument("--bucket-call", default="one", choices=["one", "per-bucket"],
+                    help="with --bucket-params: enqueue all buckets with one "
+                         "zero_shard_step_buckets call, or call zero_shard_step per bucket")
+    ap.add_argument("--scheduled", action="store_true",
+                    help="take the step constants from a device table (zero_shard_step_"
+                         "scheduled + zero_step_index_advance): with --graph every replay "
+                         "is the next step")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step's launches in a HIP graph and time its replays "
+                         "(the hyper-parameters, step t included, are fixed at capture; the "
+                         "work per replay is the step's)")
+    ap.add_argument("--probe-copy", type=int, default=1 << 32, metavar="BYTES",
+                    help="after timing, copy BYTES with the library's plain copy kernel "
+                         "(measured copy bandwidth of this GPU; the known-size kernel that "
+                         "calibrates HBM traffic counters); 0 to skip")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn the counter_collection CSVs of two rocprofv3 passes "
+                         "(--pmc FETCH_SIZE, --pmc WRITE_SIZE) over this same command into "
+                         "calibrated HBM bytes per launch, recorded in profiles/traffic.json")
+    ap.add_argument("--launch-overhead", action="store_true",
+                    help="print the per-call cost of zero_shard_step on a small shard (JSON)")
+    ap.add_argument("--chunk-sweep", metavar="LENGTHS",
+                    help="comma-separated chunk lengths: time the plain step with a table cut "
+                         "at each, round-robin over the same buffers (JSON), instead of the "
+                         "benchmark line")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="no GPU: print a markdown table of a rocprofv3 kernel trace")
+    args = ap.parse_args()
+
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return 0
+    if args.launch_overhead:
+        print(json.dumps(launch_overhead(max_chunk=args.max_chunk)), flush=True)
+        return 0
+    if args.ingest_counters:
+        rec = ingest_counters(*args.ingest_counters, W.get(args.workload), args.rank, args.state,
+                              args.probe_copy)
+        print(json.dumps(rec, indent=1))
+        return 0
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs one rank's shard step on one GPU; "
+                                   "--gpus above 1 is not supported (the collectives that "
+                                   "would feed it are out of scope)"}), flush=True)
+        return 2
+    if args.allocations < 1:
+        raise SystemExit("--allocations must be at least 1")
+
+    import torch
+
+    w = W.get(args.workload)
+    if args.chunk_sweep:
+        lengths = [int(x) for x in args.chunk_sweep.split(",")]
+        print(json.dumps(chunk_sweep(w, args, lengths)), flush=True)
+        return 0
+    r = measure_workload(w, args)
+    rec = workload_record(w, args, r)
+    out = {
+        "metric": "params updated/sec and achieved HBM GB/s (fraction of peak), fused shard step",
+        "value": rec["value"],
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": rec["config"],
+        "hbm_gbs": rec["hbm_gbs"],
+        "roofline": rec["roofline"],
+    }
+    if "extended_reduce" in rec:
+        out["extended_reduce"] = rec["extended_reduce"]
+    sec = None
+    if args.secondary != "none" and args.secondary != args.workload:
+        w2 = W.get(args.secondary)
+        r2 = measure_workload(w2, args)
+        sec = workload_record(w2, args, r2)
+        out["secondary"] = sec
     props = torch.cuda.get_device_properties(0)
     out["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                      "compute_units": props.multi_processor_count,
                      "memory_gib": round(props.total_memory / 2**30, 1)}
-    if ext is not None:
-        out["extended_reduce"] = ext
-    out["roofline"]["step_ms_median"] = step_ms[len(step_ms) // 2]
-    out["roofline"]["step_ms_min"] = step_ms[0]
     if args.probe_copy > 0:
-        out["probe_copy"] = probe_copy(args.probe_copy)
-        out["probe_read"] = probe_read(args.probe_copy)
-        out["probe_write"] = probe_write(args.probe_copy)
-        # the step's rate against the rates this GPU sustained on plain streams
-        out["roofline"]["vs_copy_probe"] = achieved / out["probe_copy"]["gbs"]
-        out["roofline"]["vs_read_probe"] = achieved / out["probe_read"]["gbs"]
-        _, rd, wr, _ = STATES[args.state]
-        gb = 2 if w.gdt == "bf16" else 4
-        rb, wb = (w.n_ranks * gb + rd) * sh.n, wr * sh.n
-        if extended and args.micro_batches > 1:
-            rb += 4 * sh.n
-        bound = mix_bound(rb, wb, out["probe_read"]["gbs"], out["probe_write"]["gbs"])
-        out["roofline"]["mix_model"] = {"read_bytes": rb, "write_bytes": wb, "bound_gbs": bound,
-                                        "frac_of_bound": achieved / bound}
+        probes = {"probe_copy": probe_copy(args.probe_copy),
+                  "probe_read": probe_read(args.probe_copy),
+                  "probe_write": probe_write(args.probe_copy)}
+        out.update(probes)
+        vendor = None
+        if not args.no_vendor_streams:
+            vendor = out["vendor_streams"] = vendor_streams(args.probe_copy, probes)
+        add_mix_model(out, w, args, r["n"], probes, vendor)
+        if sec is not None:
+            add_mix_model(sec, w2, args, r2["n"], probes, vendor)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.rank, t, args.cpu_seconds, state=args.state)
+        out["cpu_baseline"] = cpu_baseline(w, args.rank, r["next_t"], args.cpu_seconds,
+                                           sample=args.cpu_sample, state=args.state)
     print(json.dumps(out), flush=True)
     return 0
 
