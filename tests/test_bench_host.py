@@ -138,3 +138,43 @@ def test_bucket_chunk_len():
     for p in (1, 10**5, 10**6, 10**7, 10**9):
         c = bench.bucket_chunk_len(p)
         assert c in (512, 1024, 2048) and c % 64 == 0
+
+
+def test_headline_is_the_median_allocation(monkeypatch):
+    """measure_workload reports the allocation whose roofline fraction is
+    the median, with min, median and max of all of them; the JSON record's
+    value and ms_per_step are that allocation's."""
+    import argparse
+    from synth import workloads as W
+    w = W.get("gpt2")
+    n = w.shard_len
+    fr = {0: 0.70, 1: 0.76, 2: 0.73}
+
+    def fake(w_, args, alloc):
+        ms = w_.bytes_per_param() * n / (fr[alloc] * bench.HBM_PEAK_GBS * 1e9) * 1e3
+        return {"alloc": alloc, "n": n, "chunks": 7, "dst": "tensors", "max_chunk": 2048,
+                "bytes_per_param": w_.bytes_per_param(), "launches": 1, "ms_per_step": ms,
+                "kernel_ms": ms, "step_ms": [ms] * 3, "bytes_launch": w_.bytes_per_param() * n,
+                "extended": None, "next_t": 9, "achieved": fr[alloc] * bench.HBM_PEAK_GBS}
+
+    monkeypatch.setattr(bench, "time_allocation", fake)
+    args = argparse.Namespace(allocations=3, scheduled=False, state="fp32", rank=0, graph=False,
+                              bucket_params=0, bucket_call="one")
+    r = bench.measure_workload(w, args)
+    assert r["alloc"] == 2
+    fa = r["frac_by_allocation"]
+    assert (fa["min"], fa["median"], fa["max"]) == pytest.approx((0.70, 0.73, 0.76))
+    assert fa["values"] == pytest.approx([0.70, 0.76, 0.73])
+    rec = bench.workload_record(w, args, r)
+    assert rec["roofline"]["frac"] == pytest.approx(0.73)
+    assert rec["value"] == pytest.approx(n / (r["ms_per_step"] * 1e-3))
+    assert rec["config"]["workload"] == "gpt2-small rank-0 shard"
+
+
+def test_vendor_mix_bounds_use_the_best_rates():
+    """The write side of a mix bound is the faster of the write probe and the
+    vendor fill; a pure stream at the best rate sits at 1."""
+    probes = {"probe_read": {"gbs": 7000.0}, "probe_write": {"gbs": 6500.0}}
+    assert bench.best_rates(probes) == (7000.0, 6500.0)
+    assert bench.best_rates(probes, {"torch_fill_": {"gbs": 6800.0}}) == (7000.0, 6800.0)
+    assert bench.best_rates(probes, {"torch_fill_": {"gbs": 6000.0}}) == (7000.0, 6500.0)
