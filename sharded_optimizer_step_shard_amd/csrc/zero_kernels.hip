@@ -31,6 +31,7 @@ namespace zs {
 
 constexpr int kBlock = 256;       // grid-stride kernels (unfused path)
 constexpr int kStepBlock = 64;    // chunk-table kernels: one wave per workgroup
+constexpr int kStepLanes = 64;    // lanes of a wave (gfx950: wave64)
 
 // Native clang vectors: 16-byte (and 8-byte) loads and stores, and the
 // non-temporal store builtin, need them rather than HIP's struct wrappers.
@@ -418,6 +419,109 @@ __device__ __forceinline__ void store_bf16(uint16_t *dst, const uint32_t *h, boo
     }
 }
 
+// The bf16 parameter stores of one chunk.  A destination aligned for vector
+// stores gets one per lane group (store_bf16).  A misaligned one -- a tensor
+// that starts at an arbitrary element, so every group of the chunk lands
+// s0 elements short of an aligned slot -- would otherwise take VEC 2-byte
+// stores per lane.  On a chunk whose groups are all full (it starts and ends
+// on the VEC grid), the lane that owns chunk group g instead writes the
+// aligned slot that straddles groups g - 1 and g: the last VEC - s0 values of
+// group g - 1, which come from the previous lane by a wave shuffle (for
+// lane 0, from lane 63 of the previous pass), then its own first s0 values.
+// Only the chunk's first s0 elements (before its first aligned slot) and
+// its last VEC - s0 are stored element by element, by the lanes that own
+// them.  Every destination element is written exactly once.
+template <int VEC>
+struct ParamStore {
+    static constexpr int W = VEC / 2;   // 32-bit words per lane group
+    uint16_t *dst;
+    int64_t lo, hi;
+    bool vec_ok, shift;
+    int s0;                             // elements before the first aligned slot
+    uint32_t carry[W];                  // the previous pass's lane-63 group
+
+    __device__ __forceinline__ ParamStore(uint16_t *d, int64_t lo_, int64_t hi_, bool ok)
+        : dst(d), lo(lo_), hi(hi_), vec_ok(ok)
+    {
+        const int m = (int)(((uintptr_t)d >> 1) % VEC);   // elements past an aligned slot
+        shift = !ok && ((uintptr_t)d & 1) == 0 && lo % VEC == 0 && hi % VEC == 0;
+        s0 = VEC - m;
+#pragma unroll
+        for (int q = 0; q < W; ++q)
+            carry[q] = 0;
+    }
+
+    // out = values [s0, s0 + VEC) of the 2 VEC values prev ++ cur (S = s0
+    // known at compile time; s0 is uniform, so the switch below is scalar)
+    template <int S>
+    __device__ static __forceinline__ void join(uint32_t *out, const uint32_t *prev, const uint32_t *cur)
+    {
+        uint32_t all[2 * W];
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+            all[q] = prev[q];
+            all[W + q] = cur[q];
+        }
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+            constexpr int wq = S / 2;
+            if constexpr (S % 2 == 0)
+                out[q] = all[wq + q];
+            else
+                out[q] = (all[wq + q] >> 16) | (all[wq + q + 1] << 16);
+        }
+    }
+
+    // the full group starting at shard element i0, values h[0 .. VEC)
+    __device__ __forceinline__ void put(int64_t i0, const uint32_t *h)
+    {
+        uint16_t *d = dst + (i0 - lo);
+        if (!shift) {
+            store_bf16<VEC>(d, h, vec_ok);
+            return;
+        }
+        uint32_t w[W], prev[W];
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+            w[q] = h[2 * q] | (h[2 * q + 1] << 16);
+            prev[q] = __shfl_up(w[q], 1u);
+        }
+        if (threadIdx.x == 0) {
+#pragma unroll
+            for (int q = 0; q < W; ++q)
+                prev[q] = carry[q];
+        }
+#pragma unroll
+        for (int q = 0; q < W; ++q)
+            carry[q] = __shfl(w[q], kStepLanes - 1);
+        if (i0 == lo) {
+            for (int j = 0; j < s0; ++j)
+                d[j] = (uint16_t)h[j];
+        } else {
+            uint32_t o[W];
+            switch (s0) {
+            case 1: join<1>(o, prev, w); break;
+            case 2: join<2>(o, prev, w); break;
+            case 3: join<3>(o, prev, w); break;
+            case 4: if constexpr (VEC > 4) { join<4>(o, prev, w); break; } else { return; }
+            case 5: if constexpr (VEC > 5) { join<5>(o, prev, w); break; } else { return; }
+            case 6: if constexpr (VEC > 6) { join<6>(o, prev, w); break; } else { return; }
+            case 7: if constexpr (VEC > 7) { join<7>(o, prev, w); break; } else { return; }
+            default: return;
+            }
+            uint16_t *slot = d - VEC + s0;     // aligned for a VEC-element store
+            if constexpr (VEC == 8)
+                st_nt((u32x4 *)slot, (u32x4){o[0], o[1], o[2], o[3]});
+            else
+                st_nt((u32x2 *)slot, (u32x2){o[0], o[1]});
+        }
+        if (i0 + VEC == hi) {
+            for (int j = s0; j < VEC; ++j)
+                d[j] = (uint16_t)h[j];
+        }
+    }
+};
+
 // ---------------------------------------------------------------- fused step
 
 // Partial loads in flight per batch (group_sum) for each fused step, from
@@ -442,6 +546,7 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
     const int64_t g0 = lo / VEC, g1 = (hi + VEC - 1) / VEC;
     // dst address of the first element of group g0, aligned for a vector store?
     const bool vec_ok = (((uintptr_t)c.dst - (uintptr_t)(2 * (lo - g0 * VEC))) % (2 * VEC)) == 0;
+    ParamStore<VEC> ps(c.dst, lo, hi, vec_ok);
 
     for (int64_t g = g0 + threadIdx.x; g < g1; g += kStepBlock) {
         const int64_t i0 = g * VEC;
@@ -478,7 +583,7 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
             th.store(a.master + i0);
             m.store(a.m + i0);
             v.store(a.v + i0);
-            store_bf16<VEC>(d, h, vec_ok);
+            ps.put(i0, h);
         } else {
             for (int j = 0; j < VEC; ++j) {
                 const int64_t i = i0 + j;
@@ -545,6 +650,7 @@ __device__ __forceinline__ void step_chunk_m16(const StepArgs &a, const zero_chu
     const int64_t lo = c.shard_off, hi = c.shard_off + c.len;
     const int64_t g0 = lo / VEC, g1 = (hi + VEC - 1) / VEC;
     const bool vec_ok = (((uintptr_t)c.dst - (uintptr_t)(2 * (lo - g0 * VEC))) % (2 * VEC)) == 0;
+    ParamStore<VEC> ps(c.dst, lo, hi, vec_ok);
     for (int64_t g = g0 + threadIdx.x; g < g1; g += kStepBlock) {
         const int64_t i0 = g * VEC;
         uint16_t *d = c.dst + (i0 - lo);
@@ -569,7 +675,7 @@ __device__ __forceinline__ void step_chunk_m16(const StepArgs &a, const zero_chu
             th.store(a.master + i0);
             m.store(m16 + i0);
             v.store(v16 + i0);
-            store_bf16<VEC>(d, h, vec_ok);
+            ps.put(i0, h);
         } else {
             for (int j = 0; j < VEC; ++j) {
                 const int64_t i = i0 + j;
@@ -848,6 +954,7 @@ __device__ __forceinline__ void gather_chunk(const GatherArgs &a, const zero_chu
     const int64_t lo = c.shard_off, hi = c.shard_off + c.len;
     const int64_t g0 = lo / VEC, g1 = (hi + VEC - 1) / VEC;
     const bool vec_ok = (((uintptr_t)c.dst - (uintptr_t)(2 * (lo - g0 * VEC))) % (2 * VEC)) == 0;
+    ParamStore<VEC> ps(c.dst, lo, hi, vec_ok);
     for (int64_t g = g0 + threadIdx.x; g < g1; g += kStepBlock) {
         const int64_t i0 = g * VEC;
         uint16_t *d = c.dst + (i0 - lo);
@@ -858,7 +965,7 @@ __device__ __forceinline__ void gather_chunk(const GatherArgs &a, const zero_chu
 #pragma unroll
             for (int j = 0; j < VEC; ++j)
                 h[j] = to_bf16(th[j]);
-            store_bf16<VEC>(d, h, vec_ok);
+            ps.put(i0, h);
         } else {
             for (int j = 0; j < VEC; ++j) {
                 const int64_t i = i0 + j;
