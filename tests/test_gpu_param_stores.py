@@ -10,8 +10,10 @@ lane owning group g writes the aligned slot that straddles groups g - 1 and
 g); a few tensors with lengths off the group grid, and one aligned tensor,
 take the other paths beside them.  Sentinel elements between the tensors
 must survive.  Checked for the 16-byte step, the extended step, the 12-byte
-step and the unfused bf16 write, with a short table (the two-wave launch)
-and a long one (the one-wave launch)."""
+step and the unfused bf16 write, and for the pure-bf16 step (which reads and
+writes its parameters at the destinations element by element on those
+chunks), with a short table (the two-wave launch) and a long one (the
+one-wave launch)."""
 import numpy as np
 import pytest
 
@@ -141,3 +143,15 @@ def test_misaligned_parameter_stores(zs, gdt, long_table):
         assert_bitwise(got, want, f"{tag} 12-byte {what}")
     assert_bitwise(host(buf), expected_buffer(numels, offs, size, prm2),
                    f"{tag} 12-byte parameters and sentinels", strict_nan=True)
+
+    say(f"case: misaligned stores, {tag}: pure-bf16 step (parameters read and written in place)")
+    th16 = oracle.bf16_round(th0)
+    c16 = oracle.bf16_from_double(rng.standard_normal(n) * 1e-6)
+    buf.copy_(dev(expected_buffer(numels, offs, size, th16)))
+    dc, dm, dv = dev(c16), dev(m16), dev(v16)
+    zs.zero_shard_step_kahan(parts, dc, dm, dv, n, d_table, nc, hp_d)
+    th3, c3, mm3, vv3 = oracle.shard_step_kahan(parts_h, th16, c16, m16, v16, hp_h)
+    for got, want, what in ((host(dc), c3, "compensation"), (host(dm), mm3, "m"), (host(dv), vv3, "v")):
+        assert_bitwise(got, want, f"{tag} pure-bf16 {what}")
+    assert_bitwise(host(buf), expected_buffer(numels, offs, size, th3),
+                   f"{tag} pure-bf16 parameters and sentinels", strict_nan=True)
