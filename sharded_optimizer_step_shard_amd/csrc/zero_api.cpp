@@ -137,7 +137,7 @@ bool in_device_alloc(const void *p, int64_t bytes)
 
 extern "C" {
 
-int zero_version(void) { return (1 << 16) | 7; }
+int zero_version(void) { return (1 << 16) | 8; }
 
 const char *zero_strerror(int code)
 {
