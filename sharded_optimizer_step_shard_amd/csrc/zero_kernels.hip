@@ -632,8 +632,15 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
 template <zero_dtype G, int NC, bool SMALL>
 constexpr int kM16Waves = (NC > 0 && NC * Grad<G>::BYTES <= 16) ? (SMALL ? 3 : 2) : 1;
 constexpr int kKahanWaves = 3;
+// Partial-load batch of the 12-byte step: 2 with two waves per SIMD, 8 with
+// three, 16 with one (more than 16 bytes of partials per element, or N known
+// only at run time; at N = 16 bf16 that is every partial of a group at once).
+// One wave with batches of 16 against 8, one process each on three boxes,
+// 70B shard: 0.752 / 0.741 / 0.757 against 0.728 / 0.727 / 0.738; ragged fp32
+// shard (32 partials): 0.687 against 0.687.
 template <zero_dtype G, int NC, bool SMALL>
-constexpr int kM16Batch = kM16Waves<G, NC, SMALL> == 2 ? 2 : kStepBatch;
+constexpr int kM16Batch = kM16Waves<G, NC, SMALL> == 2 ? 2
+                                                       : (kM16Waves<G, NC, SMALL> == 1 ? 16 : kStepBatch);
 
 // The step on the 12-byte state: fp32 master, bf16 m and v (in a.m, a.v
 // as 16-bit patterns).  Same reduce and AdamW; the moments are read from
