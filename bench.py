@@ -14,8 +14,10 @@ default, the largest configuration that fits one GPU), the roofline block of
 the step kernel (algorithmic HBM bytes per launch / measured launch time
 against the 8 TB/s HBM peak; the median of several fresh allocations), the
 same record for a secondary workload (the Llama-7B rank-0 shard), plain
-read/write/copy streams of the library and of the vendor's libraries, and the
-CPU oracle timed on a bounded sample of the same workload on this host.
+read/write/copy streams of the library and of the vendor's libraries, the
+library's sums of 1 to 16 arrays (the rate of a mixed stream against the
+number of arrays it streams), and the CPU oracle timed on a bounded sample
+of the same workload on this host.
 
 The workload setup below (allocation, device fill, warm start) is also what
 the full-size GPU parity tests run, so they check the configuration timed
@@ -1001,6 +1003,46 @@ def vendor_streams(nbytes: int, probes: dict, reps: int = 10) -> dict:
     return out
 
 
+def sum_streams(probes: dict, vendor: dict = None, n: int = 1 << 28, ks=(1, 2, 3, 4, 8, 16),
+                reps: int = 10) -> dict:
+    """The library's sum probe (dst = src[0] + ... + src[k-1], fp32, one
+    64-lane workgroup per 1 KiB of dst) over k source arrays of n floats:
+    how the rate of a mixed stream depends on the number of arrays streamed
+    at once.  Each with its rate, fraction of the 8 TB/s peak and of its own
+    serial read/write bound from the run's best read-only and write-only
+    rates."""
+    import torch
+    import sharded_optimizer_step_shard_amd as zs
+    srcs = [torch.full((n,), float(j + 1), device="cuda") for j in range(max(ks))]
+    dst = torch.empty(n, device="cuda")
+    rates = best_rates(probes, vendor)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for k in ks:
+        def run():
+            zs.zero_probe_sum(srcs[:k], dst, n)
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        rb, wb = k * 4 * n, 4 * n
+        gbs = (rb + wb) / (ms * 1e-3) / 1e9
+        out[f"k{k}"] = {"read_bytes": rb, "write_bytes": wb, "ms": ms, "gbs": gbs,
+                        "frac_of_peak": gbs / HBM_PEAK_GBS,
+                        "frac_of_mix_bound": gbs / mix_bound(rb, wb, *rates)}
+    if not torch.equal(dst[:1024], torch.full((1024,), float(max(ks) * (max(ks) + 1) // 2),
+                                              device="cuda")):
+        raise RuntimeError("sum probe result is wrong")
+    del srcs, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -1022,7 +1064,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 30,
                     help="shard elements the CPU oracle is timed on")
-    ap.add_argument("--no-vendor-streams", action="store_true")
+    ap.add_argument("--no-vendor-streams", action="store_true",
+                    help="skip the vendor streams and the library's sum streams")
     ap.add_argument("--state", default="fp32", choices=sorted(STATES),
                     help="optimizer state: fp32 master, m, v (16 B/param ledger); fp32 "
                          "master with bf16 m, v (12 B/param ledger); or pure bf16 with a "
@@ -1131,6 +1174,7 @@ def main() -> int:
         vendor = None
         if not args.no_vendor_streams:
             vendor = out["vendor_streams"] = vendor_streams(args.probe_copy, probes)
+            out["sum_streams"] = sum_streams(probes, vendor)
         add_mix_model(out, w, args, r["n"], probes, vendor)
         if sec is not None:
             add_mix_model(sec, w2, args, r2["n"], probes, vendor)

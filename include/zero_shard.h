@@ -492,6 +492,23 @@ int zero_probe_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t mag
  */
 int zero_probe_write(void *dst, int64_t bytes, uint32_t value, hipStream_t stream);
 
+#define ZERO_PROBE_SUM_MAX 16
+
+/*
+ * Measurement aid, not part of the step: dst[i] = src[0][i] + ... +
+ * src[k-1][i] for i < n, in fp32, added in that order, with one 64-lane
+ * workgroup per 1 KiB of dst and non-temporal loads and stores.  k = 1 is a
+ * copy.  Shows how the attainable rate of a mixed stream falls as the
+ * number of arrays streamed at once grows, beside the step (which streams
+ * N partials, three state arrays in place and the parameters).
+ * src: k device pointers (host array of pointers), each 16-byte aligned and
+ * n floats long; sources may overlap each other, not dst.  dst: device,
+ * 16-byte aligned, n floats.
+ * Errors: INVALID (null, k outside 1..ZERO_PROBE_SUM_MAX, n < 0),
+ * MISALIGNED, ALIAS (dst overlaps a source), NOT_DEVICE.
+ */
+int zero_probe_sum(const float *const *src, int k, float *dst, int64_t n, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

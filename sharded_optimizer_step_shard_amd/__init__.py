@@ -33,6 +33,7 @@ ZERO_DEFAULT_MAX_CHUNK_FP32 = 1024   # fp32 partials
 # step launches up to this many chunks run at a higher occupancy
 ZERO_SMALL_LAUNCH_CHUNKS = 2048        # 16-byte and extended steps
 ZERO_SMALL_LAUNCH_CHUNKS_12B = 16384   # 12-byte step
+ZERO_PROBE_SUM_MAX = 16
 
 # Mirrors `zero_chunk` (32 bytes).
 CHUNK_DTYPE = np.dtype([("shard_off", "<i8"), ("dst", "<u8"), ("len", "<i4"),
@@ -95,6 +96,7 @@ _lib.zero_gather_write.argtypes = [_vp, _i64, _vp, _i64, _vp]
 _lib.zero_probe_copy.argtypes = [_vp, _vp, _i64, _vp]
 _lib.zero_probe_read.argtypes = [_vp, _i64, _vp, ctypes.c_uint32, _vp]
 _lib.zero_probe_write.argtypes = [_vp, _i64, ctypes.c_uint32, _vp]
+_lib.zero_probe_sum.argtypes = [_vp, _i32, _vp, _i64, _vp]
 _lib.zero_make_step_consts.argtypes = [_vp, _i64, _vp]
 _lib.zero_shard_step_scheduled.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
                                            _i64, _vp, _vp]
@@ -110,7 +112,7 @@ for _f in ("zero_build_chunks", "zero_shard_step", "zero_reduce_shard", "zero_ad
            "zero_accumulate_shard", "zero_shard_step_bf16_moments", "zero_shard_step_kahan",
            "zero_shard_step_buckets", "zero_make_step_consts", "zero_shard_step_scheduled",
            "zero_step_index_advance", "zero_shard_step_bf16_moments_scheduled",
-           "zero_shard_step_kahan_scheduled", "zero_check_chunks"):
+           "zero_shard_step_kahan_scheduled", "zero_check_chunks", "zero_probe_sum"):
     getattr(_lib, _f).restype = _i32
 
 Ptr = Union[int, "torch.Tensor", None]  # noqa: F821
@@ -386,6 +388,12 @@ def zero_probe_read(src: Ptr, nbytes: int, sink: Ptr, magic: int = 0x9E3779B9, s
 
 def zero_probe_write(dst: Ptr, nbytes: int, value: int = 0x3C003C00, stream=None) -> None:
     _check(_lib.zero_probe_write(_addr(dst), nbytes, value, _stream(stream)), "zero_probe_write")
+
+
+def zero_probe_sum(srcs: Sequence[Ptr], dst: Ptr, n: int, stream=None) -> None:
+    """dst = srcs[0] + ... + srcs[k-1] over n fp32 elements (measurement aid)."""
+    arr = (ctypes.c_void_p * max(len(srcs), 1))(*[_addr(x) for x in srcs])
+    _check(_lib.zero_probe_sum(arr, len(srcs), _addr(dst), n, _stream(stream)), "zero_probe_sum")
 
 
 def raw_call(name: str, *args) -> int:

@@ -137,7 +137,7 @@ bool in_device_alloc(const void *p, int64_t bytes)
 
 extern "C" {
 
-int zero_version(void) { return (1 << 16) | 8; }
+int zero_version(void) { return (1 << 16) | 9; }
 
 const char *zero_strerror(int code)
 {
@@ -659,6 +659,31 @@ int zero_probe_write(void *dst, int64_t bytes, uint32_t value, hipStream_t strea
     if (!in_device_alloc(dst, bytes))
         return ZERO_ERR_NOT_DEVICE;
     return hip_status(launch_probe_write(dst, bytes, value, stream));
+}
+
+int zero_probe_sum(const float *const *src, int k, float *dst, int64_t n, hipStream_t stream)
+{
+    if (!src || k < 1 || k > ZERO_PROBE_SUM_MAX || n < 0 || n > ZERO_MAX_LEN / 4 || (!dst && n > 0))
+        return ZERO_ERR_INVALID;
+    for (int j = 0; j < k; ++j)
+        if (!src[j] && n > 0)
+            return ZERO_ERR_INVALID;
+    if (!aligned16(dst))
+        return ZERO_ERR_MISALIGNED;
+    for (int j = 0; j < k; ++j)
+        if (!aligned16(src[j]))
+            return ZERO_ERR_MISALIGNED;
+    for (int j = 0; j < k; ++j)
+        if (overlaps(src[j], n * 4, dst, n * 4))
+            return ZERO_ERR_ALIAS;
+    if (n == 0)
+        return ZERO_OK;
+    if (!in_device_alloc(dst, n * 4))
+        return ZERO_ERR_NOT_DEVICE;
+    for (int j = 0; j < k; ++j)
+        if (!in_device_alloc(src[j], n * 4))
+            return ZERO_ERR_NOT_DEVICE;
+    return hip_status(launch_probe_sum(src, k, dst, n, stream));
 }
 
 }  // extern "C"

@@ -101,5 +101,6 @@ hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStrea
 hipError_t launch_probe_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t magic,
                              hipStream_t s);
 hipError_t launch_probe_write(void *dst, int64_t bytes, uint32_t value, hipStream_t s);
+hipError_t launch_probe_sum(const float *const *src, int k, float *dst, int64_t n, hipStream_t s);
 
 }  // namespace zs

