@@ -504,8 +504,9 @@ int zero_probe_write(void *dst, int64_t bytes, uint32_t value, hipStream_t strea
  * src: k device pointers (host array of pointers), each 16-byte aligned and
  * n floats long; sources may overlap each other, not dst.  dst: device,
  * 16-byte aligned, n floats.
- * Errors: INVALID (null, k outside 1..ZERO_PROBE_SUM_MAX, n < 0),
- * MISALIGNED, ALIAS (dst overlaps a source), NOT_DEVICE.
+ * Errors: INVALID (src NULL, k outside 1..ZERO_PROBE_SUM_MAX, n < 0 or
+ * above ZERO_MAX_LEN / 4, a NULL source or dst with n > 0), MISALIGNED,
+ * ALIAS (dst overlaps a source), NOT_DEVICE.  n = 0 launches nothing.
  */
 int zero_probe_sum(const float *const *src, int k, float *dst, int64_t n, hipStream_t stream);
 

@@ -121,13 +121,14 @@ __global__ __launch_bounds__(kBlock) void probe_write_kernel(u32x4 *dst, int64_t
 }
 
 // Sum streams: dst = src[0] + src[1] + ... + src[K-1] in fp32, added in that
-// order.  One 64-lane workgroup per 1 KiB lane group of dst (one-shot waves,
-// no occupancy cap), one non-temporal 16-byte load per source and one
-// non-temporal 16-byte store per lane; the floats past the last full 16-byte
-// word are summed element by element by the first workgroup.  With K = 1 it
-// is a copy.  Measured on MI355X in this shape, 1 GiB fp32 arrays: copy,
-// 2:1 and 3:1 streams at 0.80-0.85 of the 8 TB/s peak, against 0.58-0.71
-// for the same streams from the vendor's kernels.
+// order.  One 64-lane workgroup per 1 KiB lane group of dst (one-shot waves
+// up to 4M workgroups, a loop beyond; no occupancy cap), one non-temporal
+// 16-byte load per source and one non-temporal 16-byte store per lane; the
+// floats past the last full 16-byte word are summed element by element by
+// the first workgroup.  With K = 1 it is a copy.  Measured on MI355X in this
+// shape, 1 GiB fp32 arrays: copy, 2:1 and 3:1 streams at 0.77-0.85 of the
+// 8 TB/s peak, against 0.57-0.73 for the same streams from the vendor's
+// kernels; 16 sources at 0.72-0.73.
 constexpr int kSumLanes = 64;
 constexpr int64_t kSumMaxGroups = int64_t(1) << 22;
 
