@@ -527,9 +527,9 @@ struct ParamStore {
 // Partial loads in flight per batch (group_sum) for each fused step, from
 // in-process sweeps on MI355X (bitwise-equal results): batches of 8 beat 16
 // for the one-wave 16-byte step with 16 or 32 partials (70B: +1-4%, 32 fp32
-// partials: +1%); the 12-byte step running two waves per SIMD does best
-// with batches of 2 (7B: 0.665 -> 0.684 of peak); the pure-bf16 step keeps
-// 16 (smaller batches were up to 3% slower at 70B).
+// partials: +1%); the 12-byte step takes 2 with two waves per SIMD (7B:
+// 0.665 -> 0.684 of peak), 8 with three and 16 with one (kM16Batch); the
+// pure-bf16 step keeps 16 (smaller batches were up to 3% slower at 70B).
 constexpr int kStepBatch = 8;
 
 // EXT: the extended reduce of zero_shard_step_ex (two-level order, optional
@@ -778,10 +778,11 @@ void shard_step_m16_kernel(StepArgs a)
 //
 // On large launches the 16-byte step keeps at most one wave per SIMD
 // (waves_per_eu): with fewer concurrent streams the HBM sustains more of its
-// peak on this mixed read/write stream.  Measured on MI355X across chunk
-// sizes and block shapes, 4 resident waves per CU beat 8-16 (7B shard: 0.71
-// against 0.63-0.64 with two to four waves per SIMD).  Each wave still keeps
-// its group's 14 (N = 8) to 22 (N = 16) 16-byte loads in flight at once.
+// peak on this mixed read/write stream.  Measured on MI355X with occupancy
+// capped exactly by LDS reservations, one process, same buffers: 4 resident
+// waves per CU beat 3 and 5-8 (7B shard 0.721 against 0.669 and
+// 0.648-0.705; 70B 0.761 against 0.702 and 0.747-0.751).  Each wave still
+// keeps its group's 14 (N = 8) to 22 (N = 16) 16-byte loads in flight.
 //
 // KC (extended step only): -1 flat rank order, 0 two-level with the group
 // size at run time, > 0 two-level with that group size.
