@@ -940,10 +940,12 @@ def best_rates(probes: dict, vendor: dict = None) -> tuple:
 
 
 def add_mix_model(rec: dict, w: W.Workload, args, n: int, probes: dict,
-                  vendor: dict = None) -> None:
+                  vendor: dict = None, sums: dict = None) -> None:
     """The step's rate against the same run's plain-stream rates: the copy
-    and read probes, and the serial bound of its own read/write mix from the
-    best read-only and write-only rates of the run."""
+    and read probes, the serial bound of its own read/write mix from the
+    best read-only and write-only rates of the run, and (when timed) the
+    library's sums of many arrays, the attainable rate of a stream with
+    about as many arrays as the step's."""
     rl = rec["roofline"]
     achieved = rl["achieved"]
     rl["vs_copy_probe"] = achieved / probes["probe_copy"]["gbs"]
@@ -957,6 +959,8 @@ def add_mix_model(rec: dict, w: W.Workload, args, n: int, probes: dict,
     bound = mix_bound(rb, wb, read, write)
     rl["mix_model"] = {"read_bytes": rb, "write_bytes": wb, "read_gbs": read, "write_gbs": write,
                        "bound_gbs": bound, "frac_of_bound": achieved / bound}
+    if sums:
+        rl["vs_sum_streams"] = {k: achieved / v["gbs"] for k, v in sums.items() if k in ("k8", "k16")}
 
 
 def vendor_streams(nbytes: int, probes: dict, reps: int = 10) -> dict:
@@ -1175,9 +1179,9 @@ def main() -> int:
         if not args.no_vendor_streams:
             vendor = out["vendor_streams"] = vendor_streams(args.probe_copy, probes)
             out["sum_streams"] = sum_streams(probes, vendor)
-        add_mix_model(out, w, args, r["n"], probes, vendor)
+        add_mix_model(out, w, args, r["n"], probes, vendor, out.get("sum_streams"))
         if sec is not None:
-            add_mix_model(sec, w2, args, r2["n"], probes, vendor)
+            add_mix_model(sec, w2, args, r2["n"], probes, vendor, out.get("sum_streams"))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.rank, r["next_t"], args.cpu_seconds,
                                            sample=args.cpu_sample, state=args.state)

@@ -178,3 +178,25 @@ def test_vendor_mix_bounds_use_the_best_rates():
     assert bench.best_rates(probes) == (7000.0, 6500.0)
     assert bench.best_rates(probes, {"torch_fill_": {"gbs": 6800.0}}) == (7000.0, 6800.0)
     assert bench.best_rates(probes, {"torch_fill_": {"gbs": 6000.0}}) == (7000.0, 6500.0)
+
+
+def test_mix_model_and_sum_stream_ratios():
+    """The step's mix bound uses its own read and write bytes per launch (the
+    7B shard: 28 B read, 14 B written per element); the sum-stream ratios are
+    the step's rate over the 8- and 16-array sums of the same run."""
+    import types
+    w = bench.W.get("llama7b")
+    args = types.SimpleNamespace(state="fp32", micro_batches=1)
+    n = 1000
+    probes = {"probe_read": {"gbs": 7000.0}, "probe_write": {"gbs": 6000.0},
+              "probe_copy": {"gbs": 5000.0}}
+    sums = {"k1": {"gbs": 6400.0}, "k8": {"gbs": 6250.0}, "k16": {"gbs": 5000.0}}
+    rec = {"roofline": {"achieved": 5000.0}}
+    bench.add_mix_model(rec, w, args, n, probes, None, sums)
+    mm = rec["roofline"]["mix_model"]
+    assert (mm["read_bytes"], mm["write_bytes"]) == (28 * n, 14 * n)
+    assert mm["bound_gbs"] == pytest.approx(42 / (28 / 7000 + 14 / 6000))
+    assert rec["roofline"]["vs_sum_streams"] == pytest.approx({"k8": 0.8, "k16": 1.0})
+    rec2 = {"roofline": {"achieved": 5000.0}}
+    bench.add_mix_model(rec2, w, args, n, probes)
+    assert "vs_sum_streams" not in rec2["roofline"]
