@@ -534,7 +534,10 @@ constexpr int kStepBatch = 8;
 
 // EXT: the extended reduce of zero_shard_step_ex (two-level order, optional
 // accumulator of earlier micro-batches, divisor N * micro-batches).
-template <zero_dtype G, int NC, bool EXT, int KC>
+// DIV (extended step only): 1 when that divisor is a power of two (multiply
+// by its exact reciprocal), 2 otherwise (divide); 0 leaves the choice to
+// finish_reduce.
+template <zero_dtype G, int NC, bool EXT, int KC, int DIV = 0>
 __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &c,
                                            const StepScalars &k)
 {
@@ -576,7 +579,13 @@ __device__ __forceinline__ void step_chunk(const StepArgs &a, const zero_chunk &
             uint32_t h[VEC];
 #pragma unroll
             for (int j = 0; j < VEC; ++j) {
-                float gj = finish_reduce<EXT ? 0 : NC>(s[j], a.red);
+                float gj;
+                if constexpr (DIV == 1)
+                    gj = (float)(s[j] * a.red.inv_n);
+                else if constexpr (DIV == 2)
+                    gj = (float)(s[j] / a.red.n);
+                else
+                    gj = finish_reduce<EXT ? 0 : NC>(s[j], a.red);
                 adamw(gj, th[j], m[j], v[j], k);
                 h[j] = to_bf16(th[j]);
             }
@@ -806,12 +815,26 @@ void shard_step_m16_kernel(StepArgs a)
 // a SIMD's 512, so only one such wave fits.  The two-wave instance declares
 // 169 (176 allocated, two fit).  rocprofv3 reports the 257 as "132" (it
 // counts granules of 4).
+//
+// The extended step picks its divisor path once per chunk, with a uniform
+// branch around the whole chunk, instead of per element inside the unrolled
+// loop.  On MI355X, bitwise equal, same buffers: 7B 0.696 -> 0.707 (K = 4),
+// 0.648 -> 0.663 (K = 2, fold at run time), 0.697 -> 0.703 (three
+// micro-batches, so divided); 70B 0.730 -> 0.740 (K = 8).
 template <zero_dtype G, int NC, bool EXT, int KC = -1, int W = 1>
 __global__ __launch_bounds__(kStepBlock) __attribute__((amdgpu_waves_per_eu(1, W)))
 void shard_step_kernel(StepArgs a)
 {
-    for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x)
-        step_chunk<G, NC, EXT, KC>(a, chunk_at(a.chunks, ci), a.k);
+    for (int64_t ci = blockIdx.x; ci < a.n_chunks; ci += gridDim.x) {
+        if constexpr (EXT) {
+            if (a.red.pow2)
+                step_chunk<G, NC, EXT, KC, 1>(a, chunk_at(a.chunks, ci), a.k);
+            else
+                step_chunk<G, NC, EXT, KC, 2>(a, chunk_at(a.chunks, ci), a.k);
+        } else {
+            step_chunk<G, NC, EXT, KC>(a, chunk_at(a.chunks, ci), a.k);
+        }
+    }
 }
 
 // The fused steps with their constants in device memory: entry
