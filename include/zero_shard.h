@@ -56,8 +56,10 @@
  *     returns an error has launched nothing and changed nothing.  Checks,
  *     in order: null pointers and counts (INVALID), 16-byte alignment
  *     (MISALIGNED), dtype (UNSUPPORTED), overlap of inputs with outputs
- *     (ALIAS), and finally that every array range lies inside one device
- *     allocation (NOT_DEVICE, via hipMemGetAddressRange).  The chunk
+ *     (ALIAS), and finally that every array range is device memory
+ *     (NOT_DEVICE, via hipMemGetAddressRange: one allocation, or up to 65,536
+ *     physical allocations mapped back to back without a hole, as HIP's
+ *     virtual memory API and expandable-segment allocators produce).  The chunk
  *     table lives in device memory, so the step calls cannot read its dst
  *     addresses without a device round trip; zero_check_chunks checks a
  *     host table against the arrays of a step once, before the table is
@@ -135,7 +137,7 @@ enum {
     ZERO_ERR_ALIAS = 4,        /* an input array overlaps an array the call writes */
     ZERO_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
     ZERO_ERR_CAPACITY = 6,     /* caller's chunk array too small (see n_out) */
-    ZERO_ERR_NOT_DEVICE = 7    /* an array is not inside one device allocation */
+    ZERO_ERR_NOT_DEVICE = 7    /* an array range is not (wholly) device memory */
 };
 
 #define ZERO_MAX_RANKS 64

@@ -117,20 +117,37 @@ bool valid_dtype(int gdt) { return gdt == ZERO_BF16 || gdt == ZERO_FP32; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ZERO_OK : ZERO_ERR_HIP; }
 
-// [p, p + bytes) lies inside one device allocation?  Turns a stray host or
-// freed address into an error code instead of a GPU memory fault.  A failed
-// query's error is cleared so it cannot surface at the caller's next check.
+// [p, p + bytes) is device memory?  Turns a stray host or freed address
+// into an error code instead of a GPU memory fault.  Usually one allocation
+// holds the whole range (one query).  A range built from several physical
+// allocations mapped back to back (HIP's virtual memory API, allocators with
+// expandable segments) is followed mapping by mapping, each one starting
+// where the previous ends, up to kMaxMappings of them; a hole fails.  A
+// failed query's error is cleared so it cannot surface at the caller's next
+// check.
+constexpr int kMaxMappings = 1 << 16;
+
 bool in_device_alloc(const void *p, int64_t bytes)
 {
     if (bytes <= 0)
         return true;
-    hipDeviceptr_t base = nullptr;
-    size_t size = 0;
-    if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) != hipSuccess) {
-        (void)hipGetLastError();
-        return false;
+    uintptr_t at = (uintptr_t)p;
+    const uintptr_t end = at + (uint64_t)bytes;
+    for (int i = 0; i < kMaxMappings; ++i) {
+        hipDeviceptr_t base = nullptr;
+        size_t size = 0;
+        if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)at) != hipSuccess) {
+            (void)hipGetLastError();
+            return false;
+        }
+        const uintptr_t b0 = (uintptr_t)base, b1 = b0 + size;
+        if (at < b0 || at >= b1)
+            return false;
+        if (end <= b1)
+            return true;
+        at = b1;
     }
-    return (uintptr_t)p >= (uintptr_t)base && (uintptr_t)p + (uint64_t)bytes <= (uintptr_t)base + size;
+    return false;
 }
 
 }  // namespace
@@ -149,7 +166,7 @@ const char *zero_strerror(int code)
     case ZERO_ERR_ALIAS: return "input overlaps an output";
     case ZERO_ERR_HIP: return "HIP launch error";
     case ZERO_ERR_CAPACITY: return "chunk array too small";
-    case ZERO_ERR_NOT_DEVICE: return "array not inside one device allocation";
+    case ZERO_ERR_NOT_DEVICE: return "array range is not device memory";
     default: return "unknown error code";
     }
 }
