@@ -49,6 +49,11 @@
  *   - All array arguments are device pointers unless stated otherwise.
  *     The caller owns all memory.  The library never allocates or frees
  *     device memory and keeps no global mutable state; calls are re-entrant.
+ *   - Kernels run on the device that `stream` belongs to (the current
+ *     device for the null stream).  Every array must be accessible from that
+ *     device: its own memory, or a peer's mapped with peer access or an IPC
+ *     handle.  The checks confirm that an address range is device memory,
+ *     not which device holds it.
  *   - Work is enqueued on `stream` (0 = the null stream) and the call
  *     returns without synchronising.  Device faults surface at the caller's
  *     next synchronisation, as usual for HIP.
