@@ -75,18 +75,23 @@ class Mapped:
         base = ctypes.c_void_p()
         assert h.hipMemAddressReserve(ctypes.byref(base), self.size, PIECE, None, 0) == 0
         self.base = base.value
-        self.handles = []
+        self.handles = []          # (handle, mapped) per piece; None for the hole
         acc = AccessDesc(location=MemLocation(1, 0), flags=3)
-        for i in range(pieces):
-            if i == hole:
-                self.handles.append(None)
-                continue
-            hd = ctypes.c_void_p()
-            assert h.hipMemCreate(ctypes.byref(hd), PIECE, ctypes.byref(self.prop), 0) == 0
-            self.handles.append(hd.value)
-            at = self.base + i * PIECE
-            assert h.hipMemMap(at, PIECE, 0, hd.value, 0) == 0
-            assert h.hipMemSetAccess(at, PIECE, ctypes.byref(acc), 1) == 0
+        try:
+            for i in range(pieces):
+                if i == hole:
+                    self.handles.append(None)
+                    continue
+                hd = ctypes.c_void_p()
+                assert h.hipMemCreate(ctypes.byref(hd), PIECE, ctypes.byref(self.prop), 0) == 0
+                self.handles.append([hd.value, False])
+                at = self.base + i * PIECE
+                assert h.hipMemMap(at, PIECE, 0, hd.value, 0) == 0
+                self.handles[-1][1] = True
+                assert h.hipMemSetAccess(at, PIECE, ctypes.byref(acc), 1) == 0
+        except BaseException:
+            self.free()
+            raise
 
     def upload(self, a: np.ndarray):
         assert a.nbytes <= self.size
@@ -96,11 +101,17 @@ class Mapped:
         assert self.h.hipMemcpy(a.ctypes.data, self.base, a.nbytes, 2) == 0     # device to host
 
     def free(self):
-        for i, hd in enumerate(self.handles):
-            if hd is not None:
-                assert self.h.hipMemUnmap(self.base + i * PIECE, PIECE) == 0
-                assert self.h.hipMemRelease(hd) == 0
-        assert self.h.hipMemAddressFree(self.base, self.size) == 0
+        ok = True
+        for i, e in enumerate(self.handles):
+            if e is None:
+                continue
+            hd, mapped = e
+            if mapped:
+                ok &= self.h.hipMemUnmap(self.base + i * PIECE, PIECE) == 0
+            ok &= self.h.hipMemRelease(hd) == 0
+        self.handles = []
+        ok &= self.h.hipMemAddressFree(self.base, self.size) == 0
+        assert ok
 
 
 def test_step_on_arrays_mapped_from_several_allocations(hip):
